@@ -1,0 +1,302 @@
+/*
+ * lco.c -- plain serial CPU oracle for the Lion Cub compressed-update step.
+ *
+ * TEST INFRASTRUCTURE ONLY (see lco.h): loaded by the tests, the smoke check
+ * and the benchmark's CPU-baseline leg, never by the GPU library.
+ *
+ * Build: gcc -std=c11 -O2 -ffp-contract=off -fno-fast-math -fPIC -shared
+ *
+ * Each function cites the passage it follows.  [LC] is the pith.science
+ * review page of "Lion Cub: Minimizing Communication Overhead in Distributed
+ * Lion"; [DL] is the atlas.scime.ai summary page of "Communication Efficient
+ * Distributed Training with Distributed Lion".
+ *
+ * Parity pins (tests/test_oracle_pins.py): Lion closed forms, hand-worked
+ * pack/vote/quantisation examples, brute force over all sign patterns for
+ * W <= 5, exact rational arithmetic for Eq. (1) and for exactly summable
+ * mean-|x| inputs, the summation error bound for the rest, invariants, and
+ * torch's bf16 conversion.  The fixed order of the mean-|x| tree is a
+ * definition of this project (the pages only say "mean absolute value"):
+ * beyond the exact-sum cases and the error bound it is parity unpinned.
+ */
+#include "lco.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ---------------------------------------------------------------- bf16 -- */
+
+float lco_bf16_to_f32(uint16_t b) {
+  uint32_t u = (uint32_t)b << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return f;
+}
+
+uint16_t lco_f32_to_bf16(float f) {
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0; /* NaN */
+  /* round to nearest, ties to even, on the 16 dropped bits */
+  uint32_t lsb = (u >> 16) & 1u;
+  return (uint16_t)((u + 0x7FFFu + lsb) >> 16);
+}
+
+static float load_g(const lco_cfg *cfg, const void *g, int64_t k) {
+  if (cfg->grad_bf16) return lco_bf16_to_f32(((const uint16_t *)g)[k]);
+  return ((const float *)g)[k];
+}
+
+/* tensor holding element j (linear search: plain, not fast) */
+static int32_t tensor_of(const lco_cfg *cfg, int64_t j) {
+  int32_t T = 0;
+  while (T + 1 < cfg->n_tensors && cfg->off[T + 1] <= j) T++;
+  return T;
+}
+
+/* ------------------------------------------------- 1-bit compression [LC] */
+
+/* [LC] "What carries the argument": signs packed as 0/1, exact zeros forced
+ * to +1 or -1 on alternating iterations; the assumptions list fixes the order
+ * (+1 on odd, -1 on even iterations).  t counts steps from 1.  Anything that
+ * is neither > 0 nor < 0 (+0, -0, NaN) is treated as an exact zero. */
+int lco_bit(float c, int64_t t) {
+  if (c > 0.0f) return 1;
+  if (c < 0.0f) return 0;
+  return (int)(t & 1);
+}
+
+void lco_pack(int32_t W, int64_t d, int64_t ld, const float *x, int64_t t,
+              uint64_t *bits) {
+  int64_t words = ld / 64;
+  for (int32_t i = 0; i < W; i++) {
+    for (int64_t k = 0; k < words; k++) bits[i * words + k] = 0;
+    for (int64_t j = 0; j < d; j++) {
+      if (lco_bit(x[i * ld + j], t))
+        bits[i * words + j / 64] |= (uint64_t)1 << (j % 64);
+    }
+  }
+}
+
+/* [LC] majority vote of the workers' signs; [DL] "Approach" (MaVo).  A tie
+ * (2*count == W) is the zero that a 1-bit result cannot carry, so it follows
+ * the same parity rule as an exact zero of c (LCO_TIE_PARITY), or stays 0
+ * (LCO_TIE_ZERO). */
+static int8_t vote_sign(int32_t W, int32_t count, int64_t t, int32_t tie_mode) {
+  if (2 * count > W) return 1;
+  if (2 * count < W) return -1;
+  if (tie_mode == LCO_TIE_ZERO) return 0;
+  return (t & 1) ? 1 : -1;
+}
+
+void lco_vote(int32_t W, int64_t d, int64_t ld, const uint64_t *bits,
+              int64_t t, int32_t tie_mode, uint8_t *counts, int8_t *sign) {
+  int64_t words = ld / 64;
+  for (int64_t j = 0; j < d; j++) {
+    int32_t v = 0;
+    for (int32_t i = 0; i < W; i++)
+      v += (int32_t)((bits[i * words + j / 64] >> (j % 64)) & 1u);
+    if (counts) counts[j] = (uint8_t)v;
+    if (sign) sign[j] = vote_sign(W, v, t, tie_mode);
+  }
+}
+
+/* -------------------------------------------------- mean |x| (Eq. (1) M1) */
+
+/* [LC] Eq. (1): M1 is the mean absolute value.  Summation order (D-M1, a
+ * definition of this project so that any two implementations agree bit for
+ * bit): a row is cut into blocks of 4096; in a block, lane l (0..255) takes
+ * four rounds r, each over the four consecutive values at 1024*r + 4*l,
+ * accumulating acc += ((e0 + e1) + (e2 + e3)) in fp64 from acc = 0; each group
+ * of 64 lanes is folded by halving (a[q] += a[q+s] for s = 32, 16, .., 1); the
+ * block partial is (w0 + w1) + (w2 + w3) over its four groups. */
+static double fold64(double *a) {
+  for (int s = LCO_M1_WAVE / 2; s >= 1; s /= 2)
+    for (int q = 0; q < s; q++) a[q] = a[q] + a[q + s];
+  return a[0];
+}
+
+double lco_m1_block(const float *a, int64_t n) {
+  double acc[LCO_M1_LANES];
+  for (int l = 0; l < LCO_M1_LANES; l++) {
+    acc[l] = 0.0;
+    for (int r = 0; r < 4; r++) {
+      double e[4];
+      for (int k = 0; k < 4; k++) {
+        int64_t idx = 1024 * r + 4 * l + k;
+        e[k] = idx < n ? fabs((double)a[idx]) : 0.0;
+      }
+      acc[l] = acc[l] + ((e[0] + e[1]) + (e[2] + e[3]));
+    }
+  }
+  double wv[4];
+  for (int w = 0; w < 4; w++) wv[w] = fold64(acc + LCO_M1_WAVE * w);
+  return (wv[0] + wv[1]) + (wv[2] + wv[3]);
+}
+
+/* Finalize: lane l (0..63) sums the partials of blocks l, l+64, l+128, ...
+ * in increasing order from 0.0, the 64 lane sums are folded as above, and
+ * the total is divided by the element count. */
+double lco_m1_finalize(const double *P, int64_t nb, int64_t nT) {
+  double p[LCO_M1_WAVE];
+  for (int l = 0; l < LCO_M1_WAVE; l++) {
+    p[l] = 0.0;
+    for (int64_t b = l; b < nb; b += LCO_M1_WAVE) p[l] = p[l] + P[b];
+  }
+  return fold64(p) / (double)nT;
+}
+
+double lco_m1(const float *x, int64_t n) {
+  int64_t nb = (n + LCO_M1_BLOCK - 1) / LCO_M1_BLOCK;
+  double *P = (double *)malloc((size_t)(nb > 0 ? nb : 1) * sizeof(double));
+  for (int64_t b = 0; b < nb; b++) {
+    int64_t len = n - b * LCO_M1_BLOCK;
+    if (len > LCO_M1_BLOCK) len = LCO_M1_BLOCK;
+    P[b] = lco_m1_block(x + b * LCO_M1_BLOCK, len);
+  }
+  double M = lco_m1_finalize(P, nb, n);
+  free(P);
+  return M;
+}
+
+/* [LC] Eq. (1): Q1(x) = clamp(round((2^(n-1)-1) * x / M1(x)), 2^(n-1)-1).
+ * Readings: the clamp is symmetric, [-Qmax, +Qmax]; round is deterministic
+ * half-to-even; the scale Qmax/M1 and the product c*scale are fp64; a row
+ * with M1 == 0 (all zeros) gives all-zero codes. */
+int8_t lco_q1(float c, double m1, int32_t qbits) {
+  int32_t qmax = (1 << (qbits - 1)) - 1;
+  if (m1 == 0.0) return 0;
+  double scale = (double)qmax / m1;
+  double r = rint((double)c * scale);
+  if (r > (double)qmax) r = (double)qmax;
+  if (r < -(double)qmax) r = -(double)qmax;
+  return (int8_t)r;
+}
+
+void lco_quant_l1(const lco_cfg *cfg, int64_t ld, const float *x,
+                  int8_t *codes, double *m1) {
+  for (int32_t i = 0; i < cfg->W; i++) {
+    for (int32_t T = 0; T < cfg->n_tensors; T++) {
+      int64_t a = cfg->off[T], n = cfg->off[T + 1] - cfg->off[T];
+      double M = lco_m1(x + i * ld + a, n);
+      if (m1) m1[(int64_t)i * cfg->n_tensors + T] = M;
+      for (int64_t j = a; j < a + n; j++)
+        codes[i * ld + j] = lco_q1(x[i * ld + j], M, cfg->qbits);
+    }
+  }
+}
+
+/* ------------------------------------------------------------- the step -- */
+
+/* [LC] "What carries the argument": c_{i,t} = beta1*m_{i,t-1} +
+ * (1-beta1)*grad f_i(theta_{t-1}).  (1-beta1) is formed once in fp32. */
+void lco_c_row(const lco_cfg *cfg, int64_t n, const float *m, const void *g,
+               float *c) {
+  float omega1 = 1.0f - cfg->beta1;
+  for (int64_t k = 0; k < n; k++)
+    c[k] = (cfg->beta1 * m[k]) + (omega1 * load_g(cfg, g, k));
+}
+
+void lco_m1_all(const lco_cfg *cfg, int64_t ld, const float *m, const void *g,
+                double *m1) {
+  size_t gsz = cfg->grad_bf16 ? 2 : 4;
+  float *c = (float *)malloc((size_t)(cfg->d > 0 ? cfg->d : 1) * sizeof(float));
+  for (int32_t i = 0; i < cfg->W; i++) {
+    lco_c_row(cfg, cfg->d, m + i * ld, (const char *)g + (size_t)(i * ld) * gsz, c);
+    for (int32_t T = 0; T < cfg->n_tensors; T++) {
+      int64_t a = cfg->off[T], n = cfg->off[T + 1] - cfg->off[T];
+      m1[(int64_t)i * cfg->n_tensors + T] = lco_m1(c + a, n);
+    }
+  }
+  free(c);
+}
+
+/* One element column j: every worker's c from the pre-step m, compression,
+ * aggregation, the global sign applied to theta (decoupled weight decay, the
+ * Lion rule), then each worker's momentum update and, on averaging steps for
+ * designated tensors, the worker mean of the new momenta ([LC] selective
+ * momentum synchronisation of the input-embedding and output layers; the
+ * interval is the sync_every parameter, 10 in the pages' runs). */
+void lco_step_range(const lco_cfg *cfg, int64_t j0, int64_t j1,
+                    const double *m1, void *theta, float *m, const void *g,
+                    int64_t ldc, int64_t t, const lco_debug *dbg) {
+  const int32_t W = cfg->W;
+  const float omega1 = 1.0f - cfg->beta1;
+  const float omega2 = 1.0f - cfg->beta2;
+  const int avg_step = (t % cfg->sync_every) == 0;
+  const int64_t words = ldc / 64;
+
+  if (dbg && dbg->bits)
+    for (int64_t k = 0; k < (int64_t)W * words; k++) dbg->bits[k] = 0;
+
+  int32_t T = tensor_of(cfg, j0);
+  for (int64_t j = j0; j < j1; j++) {
+    const int64_t col = j - j0;
+    while (T + 1 < cfg->n_tensors && cfg->off[T + 1] <= j) T++;
+
+    /* 1-2: c per worker, compressed; 3: aggregated */
+    int32_t count = 0, sum = 0;
+    for (int32_t i = 0; i < W; i++) {
+      float G = load_g(cfg, g, i * ldc + col);
+      float c = (cfg->beta1 * m[i * ldc + col]) + (omega1 * G);
+      if (cfg->agg == LCO_AGG_VOTE) {
+        int b = lco_bit(c, t);
+        count += b;
+        if (dbg && dbg->bits && b)
+          dbg->bits[i * words + col / 64] |= (uint64_t)1 << (col % 64);
+      } else {
+        int8_t q = lco_q1(c, m1[(int64_t)i * cfg->n_tensors + T], cfg->qbits);
+        sum += q;
+        if (dbg && dbg->codes) dbg->codes[i * ldc + col] = q;
+      }
+    }
+    int8_t s;
+    if (cfg->agg == LCO_AGG_VOTE) {
+      s = vote_sign(W, count, t, cfg->tie_mode);
+    } else {
+      /* [LC]: a global sign of the integer sum; the p-bit sum can carry
+       * zero, so sgn(0) = 0 and the parameter only decays. */
+      s = (int8_t)((sum > 0) - (sum < 0));
+    }
+    if (dbg && dbg->counts) dbg->counts[col] = (uint8_t)count;
+    if (dbg && dbg->sums) dbg->sums[col] = sum;
+    if (dbg && dbg->sign) dbg->sign[col] = s;
+
+    /* 4: theta <- theta - lr*(sign + wd*theta) */
+    float sf = (float)s;
+    if (cfg->theta_bf16) {
+      uint16_t *th = (uint16_t *)theta;
+      float x = lco_bf16_to_f32(th[col]);
+      float y = x - (cfg->lr * (sf + (cfg->wd * x)));
+      th[col] = lco_f32_to_bf16(y);
+    } else {
+      float *th = (float *)theta;
+      float x = th[col];
+      th[col] = x - (cfg->lr * (sf + (cfg->wd * x)));
+    }
+
+    /* 5: m_i <- beta2*m_i + (1-beta2)*g_i, then optional worker mean */
+    for (int32_t i = 0; i < W; i++) {
+      float G = load_g(cfg, g, i * ldc + col);
+      m[i * ldc + col] = (cfg->beta2 * m[i * ldc + col]) + (omega2 * G);
+    }
+    if (avg_step && cfg->sync_m && cfg->sync_m[T]) {
+      float acc = m[col];
+      for (int32_t i = 1; i < W; i++) acc = acc + m[i * ldc + col];
+      float avg = acc / (float)W;
+      for (int32_t i = 0; i < W; i++) m[i * ldc + col] = avg;
+    }
+  }
+}
+
+void lco_step(const lco_cfg *cfg, int64_t ld, void *theta, float *m,
+              const void *g, int64_t t, const lco_debug *dbg) {
+  double *m1 = 0;
+  if (cfg->agg == LCO_AGG_L1SUM) {
+    m1 = (double *)malloc((size_t)cfg->W * cfg->n_tensors * sizeof(double));
+    lco_m1_all(cfg, ld, m, g, m1);
+  }
+  lco_step_range(cfg, 0, cfg->d, m1, theta, m, g, ld, t, dbg);
+  free(m1);
+}

@@ -1,0 +1,133 @@
+/*
+ * lco.h -- plain serial CPU oracle for the Lion Cub compressed-update step.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This library defines, in slow and obviously
+ * correct loops, what the GPU library computes.  Only the test-suite, the
+ * smoke check and the benchmark's CPU-baseline leg may load it.  It shares no
+ * source, header, table or helper with the GPU library, and the GPU library
+ * never calls it.
+ *
+ * Sources (the web pages this method is described on):
+ *   [LC]  "Lion Cub: Minimizing Communication Overhead in Distributed Lion",
+ *         pith.science review page: section "What carries the argument"
+ *         (the pre-sign update vector c_{i,t}, the 0/1 sign packing with
+ *         exact zeros alternated by iteration parity, Eq. (1) L1
+ *         quantisation), "Core claim", the assumptions list ("alternating
+ *         0 to +1 or -1 on odd and even iterations"), Figure 1 and
+ *         Figure 10 captions, and the reference-graph note that with 4
+ *         workers over 30% of majority votes tie.
+ *   [DL]  "Communication Efficient Distributed Training with Distributed
+ *         Lion", atlas.scime.ai summary page: section "Approach" (each worker
+ *         keeps its own momentum; majority vote / averaging of the binary
+ *         update vectors).
+ * The Lion update and momentum rules themselves (theta -= lr*(sign+wd*theta),
+ * m = beta2*m + (1-beta2)*g) are the standard Lion optimizer the Lion Cub page
+ * builds on (its reference "Symbolic Discovery of Optimization Algorithms").
+ *
+ * Every floating-point expression below is evaluated exactly as written, one
+ * IEEE operation at a time, round-to-nearest-even, no contraction into FMA,
+ * subnormals kept (build with -O2 -ffp-contract=off -fno-fast-math).
+ *
+ * Parity status of each function is stated beside it.
+ */
+#ifndef LCO_H
+#define LCO_H
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { LCO_AGG_VOTE = 0, LCO_AGG_L1SUM = 1 };
+enum { LCO_TIE_PARITY = 0, LCO_TIE_ZERO = 1 };
+
+/* Block / lane constants of the fixed mean-|x| summation tree (D-M1). */
+enum { LCO_M1_BLOCK = 4096, LCO_M1_LANES = 256, LCO_M1_WAVE = 64 };
+
+typedef struct {
+  int64_t d;               /* parameters per worker                        */
+  int32_t W;               /* simulated workers                            */
+  int32_t n_tensors;       /* tensors in the flat parameter vector         */
+  const int64_t *off;      /* n_tensors+1 ascending offsets, off[0]=0, off[n]=d */
+  const uint8_t *sync_m;   /* n_tensors flags (momentum averaged) or NULL  */
+  int32_t sync_every;      /* averaging on steps with t % sync_every == 0  */
+  int32_t theta_bf16;      /* theta stored as bf16 (else fp32)             */
+  int32_t grad_bf16;       /* g stored as bf16 (else fp32)                 */
+  int32_t agg;             /* LCO_AGG_VOTE or LCO_AGG_L1SUM                */
+  int32_t qbits;           /* n of Eq. (1), 2..8, L1 path only             */
+  int32_t tie_mode;        /* LCO_TIE_PARITY or LCO_TIE_ZERO, vote path    */
+  float beta1, beta2, lr, wd;
+} lco_cfg;
+
+/* bf16 <-> fp32: widening is exact; narrowing rounds to nearest-even,
+ * NaN -> 0x7FC0.  Pinned against torch's fp32->bf16 conversion. */
+float    lco_bf16_to_f32(uint16_t b);
+uint16_t lco_f32_to_bf16(float f);
+
+/* [LC] sign packing: 1 for c > 0, 0 for c < 0, exact zero (either sign)
+ * takes the step parity: 1 on odd t, 0 on even t. */
+int lco_bit(float c, int64_t t);
+
+/* Pack x[W][ld] (first d of each row used) into bits[W][ld/64]: element j of
+ * worker i is bit j%64 of word i*(ld/64) + j/64; bits at j >= d are 0. */
+void lco_pack(int32_t W, int64_t d, int64_t ld, const float *x, int64_t t,
+              uint64_t *bits);
+
+/* Majority vote over the W bitmaps.  counts[j] = number of 1 bits; sign[j]
+ * = +1 if 2*counts > W, -1 if 2*counts < W; a tie takes the step parity
+ * (+1 odd t, -1 even t) under LCO_TIE_PARITY or 0 under LCO_TIE_ZERO.
+ * Either output may be NULL. */
+void lco_vote(int32_t W, int64_t d, int64_t ld, const uint64_t *bits,
+              int64_t t, int32_t tie_mode, uint8_t *counts, int8_t *sign);
+
+/* Fixed-order fp64 sum of |a| over one block of n <= 4096 values (D-M1
+ * block partial).  Values past n count as +0.0. */
+double lco_m1_block(const float *a, int64_t n);
+
+/* M1 from the nb block partials of one (worker, tensor) of nT elements. */
+double lco_m1_finalize(const double *P, int64_t nb, int64_t nT);
+
+/* M1 of one row of n values (block partials + finalize). */
+double lco_m1(const float *x, int64_t n);
+
+/* Eq. (1) code of one value given the row's M1 and n = qbits. */
+int8_t lco_q1(float c, double m1, int32_t qbits);
+
+/* Standalone L1 quantisation of x[W][ld]: codes[W][ld] (first d of each row
+ * written) and, if m1 != NULL, m1[W][n_tensors]. */
+void lco_quant_l1(const lco_cfg *cfg, int64_t ld, const float *x,
+                  int8_t *codes, double *m1);
+
+/* c = beta1*m + (1-beta1)*G for n elements of one worker row (G = g widened
+ * to fp32). */
+void lco_c_row(const lco_cfg *cfg, int64_t n, const float *m, const void *g,
+               float *c);
+
+/* M1 of every (worker, tensor) from the full state: m1[W][n_tensors]. */
+void lco_m1_all(const lco_cfg *cfg, int64_t ld, const float *m, const void *g,
+                double *m1);
+
+/* Optional per-element outputs of a step (any member may be NULL). */
+typedef struct {
+  uint64_t *bits;   /* [W][ldc/64]; needs j0 % 64 == 0 and ldc % 64 == 0 */
+  int8_t   *codes;  /* [W][ldc]                                          */
+  uint8_t  *counts; /* [j1-j0]                                           */
+  int32_t  *sums;   /* [j1-j0]                                           */
+  int8_t   *sign;   /* [j1-j0]                                           */
+} lco_debug;
+
+/* One step over the element range [j0, j1).  Chunk layout: element j of
+ * worker i lives at m[i*ldc + (j-j0)], g likewise, theta at theta[j-j0].
+ * m1 is m1[W][n_tensors] (L1 path; may be NULL on the vote path). */
+void lco_step_range(const lco_cfg *cfg, int64_t j0, int64_t j1,
+                    const double *m1, void *theta, float *m, const void *g,
+                    int64_t ldc, int64_t t, const lco_debug *dbg);
+
+/* One whole step in place on the full state (theta[d], m[W][ld], g[W][ld]). */
+void lco_step(const lco_cfg *cfg, int64_t ld, void *theta, float *m,
+              const void *g, int64_t t, const lco_debug *dbg);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

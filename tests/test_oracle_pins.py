@@ -1,0 +1,503 @@
+"""Pins of the CPU oracle to facts that do not come from the oracle itself.
+
+Each test names what it pins the oracle to: a closed form of the Lion
+recurrence, a hand-worked example from the definitions on the Lion Cub page
+(pith.science review, "What carries the argument" and Eq. (1)), brute force
+over every sign pattern, exact rational arithmetic, a library routine (NumPy's
+bit packing, Python's correctly rounded math.fsum, torch's bf16 conversion),
+an invariant, or a statistical property the pages state (the majority-vote tie
+rate).  No expected value here is produced by the GPU library.
+"""
+import itertools
+import math
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from synth import workloads as wls
+from synth.gen import bf16_bits_to_f32
+
+
+def one_tensor(d, W, **kw):
+    return wls.flat("pin", d, W=W, **kw)
+
+
+# ------------------------------------------------------------------ bf16 --
+
+def test_bf16_rounding_matches_torch(oracle):
+    """fp32 -> bf16 round-to-nearest-even equals torch's conversion."""
+    import torch
+    rs = np.random.default_rng(1)
+    bits = rs.integers(0, 2**32, 20000, dtype=np.uint64).astype(np.uint32)
+    bits = bits[(bits & 0x7F800000) != 0x7F800000]            # finite only
+    ties = (rs.integers(0, 2**16, 2000, dtype=np.uint32) << 16) | 0x8000
+    ties = ties[(ties & 0x7F800000) != 0x7F800000]
+    edge = np.array([0x00000000, 0x80000000, 0x7F7FFFFF, 0xFF7FFFFF, 0x00000001,
+                     0x00008000, 0x00018000, 0x3F808000, 0x3F818000], dtype=np.uint32)
+    allb = np.concatenate([bits, ties, edge])
+    f = allb.view(np.float32)
+    want = torch.from_numpy(f.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = oracle.f32_to_bf16(f)
+    assert np.array_equal(got, want)
+    # specials
+    L = oracle.lib()
+    assert L.lco_f32_to_bf16(float("inf")) == 0x7F80
+    assert L.lco_f32_to_bf16(float("-inf")) == 0xFF80
+    assert L.lco_f32_to_bf16(float("nan")) == 0x7FC0
+    assert L.lco_bf16_to_f32(0x3F80) == 1.0
+
+
+# ------------------------------------------------------ 1-bit compression --
+
+def test_bit_rule_zero_parity(oracle):
+    """Signs packed as 0/1; an exact zero becomes +1 on odd and -1 on even
+    iterations (Lion Cub page, "What carries the argument" and the
+    alternating-sign assumption)."""
+    for t in (1, 2, 3, 4, 101, 1000):
+        assert oracle.bit(0.5, t) == 1
+        assert oracle.bit(-1e-30, t) == 0
+        assert oracle.bit(1e-45, t) == 1            # subnormal is not zero
+        z = 1 if t % 2 == 1 else 0
+        assert oracle.bit(0.0, t) == z
+        assert oracle.bit(-0.0, t) == z
+
+
+# Hand-worked from the definitions (W=4, d=8).  t=1: zeros -> 1; t=2: zeros -> 0.
+B1_X = np.array([
+    [0.5, -0.1, 0.0, 2.0, -3.0, 0.0, 1e-9, -1e-9],
+    [0.2, 0.3, -0.4, -2.0, -1.0, 0.0, 0.0, 0.7],
+    [-0.1, 0.2, 0.0, 1.0, 0.5, 0.0, -2.0, 0.1],
+    [-0.3, -0.5, 0.1, -1.0, -0.2, 0.0, 0.3, 0.0],
+], dtype=np.float32)
+B1 = {
+    1: dict(bytes=[0x6D, 0xE3, 0xBE, 0xE4], counts=[2, 2, 3, 2, 1, 4, 3, 3],
+            parity=[1, 1, 1, 1, -1, 1, 1, 1], zero=[0, 0, 1, 0, -1, 1, 1, 1]),
+    2: dict(bytes=[0x49, 0x83, 0x9A, 0x44], counts=[2, 2, 1, 2, 1, 0, 2, 2],
+            parity=[-1] * 8, zero=[0, 0, -1, 0, -1, -1, 0, 0]),
+}
+
+
+@pytest.mark.parametrize("t", [1, 2])
+def test_pack_vote_handworked(oracle, t):
+    x = np.zeros((4, 64), dtype=np.float32)
+    x[:, :8] = B1_X
+    bits = oracle.pack(x, 8, t)
+    assert bits.shape == (4, 1)
+    assert [int(w) for w in bits[:, 0]] == B1[t]["bytes"]
+    counts, sign = oracle.vote(bits, 4, 8, t, oracle.TIE_PARITY)
+    assert counts.tolist() == B1[t]["counts"]
+    assert sign.tolist() == B1[t]["parity"]
+    counts, sign = oracle.vote(bits, 4, 8, t, oracle.TIE_ZERO)
+    assert sign.tolist() == B1[t]["zero"]
+
+
+@pytest.mark.parametrize("t", [1, 2])
+def test_pack_layout_matches_numpy_packbits(oracle, t):
+    """LSB-first little-endian u64 words, bits past d zero: the layout equals
+    NumPy's packbits(bitorder='little') of the 0/1 sign vector."""
+    rs = np.random.default_rng(7)
+    W, d, ld = 3, 200, 256
+    x = rs.standard_normal((W, ld)).astype(np.float32)
+    x[rs.random((W, ld)) < 0.1] = 0.0
+    x[0, 5] = -0.0
+    bits = oracle.pack(x, d, t)
+    sgn = (x > 0) | ((x == 0) & (t % 2 == 1))
+    sgn[:, d:] = False
+    want = np.packbits(sgn, axis=1, bitorder="little").view("<u8")
+    assert np.array_equal(bits, want)
+
+
+@pytest.mark.parametrize("W", [1, 2, 3, 4, 5])
+def test_vote_bruteforce_all_sign_patterns(oracle, W):
+    """Every pattern of c in {-1, 0, +1}^W: the vote equals the sign of the
+    sum of +-1 votes (zeros voted by parity), a zero sum (a tie) resolved by
+    the tie rule.  Computed by +-1 arithmetic, not by counting bits."""
+    pats = np.array(list(itertools.product([-1.0, 0.0, 1.0], repeat=W)), dtype=np.float32)
+    for t in (1, 2, 3, 4):
+        for tie in (oracle.TIE_PARITY, oracle.TIE_ZERO):
+            for a in range(0, len(pats), 64):
+                chunk = pats[a:a + 64]
+                d = len(chunk)
+                x = np.zeros((W, 64), dtype=np.float32)
+                x[:, :d] = chunk.T
+                bits = oracle.pack(x, d, t)
+                counts, sign = oracle.vote(bits, W, d, t, tie)
+                for k in range(d):
+                    votes = [1 if v > 0 else -1 if v < 0 else (1 if t % 2 else -1)
+                             for v in chunk[k]]
+                    S = sum(votes)
+                    assert counts[k] == votes.count(1)
+                    if S != 0:
+                        exp = 1 if S > 0 else -1
+                    else:
+                        exp = 0 if tie == oracle.TIE_ZERO else (1 if t % 2 else -1)
+                    assert sign[k] == exp, (W, t, tie, chunk[k])
+
+
+# ------------------------------------------------- Lion closed forms -------
+
+def _run(oracle, wl, theta, m, g_fn, steps, debug=False):
+    out = []
+    for t in range(1, steps + 1):
+        g = g_fn(t)
+        dbg = oracle.step(wl, theta, m, g, t, debug=debug)
+        out.append(dbg)
+    return out
+
+
+@pytest.mark.parametrize("agg", ["vote", "l1"])
+def test_lion_closed_form_identical_workers(oracle, agg):
+    """W identical workers, m0 = 0, constant g: c_1 = (1-b1) g, every worker
+    agrees, the global sign is sgn(g) every step, and the recurrence has the
+    closed forms theta_t = a^t theta_0 - sgn(g) (1 - a^t) / wd with
+    a = 1 - lr*wd, and m_t = (1 - b2^t) g.  On the L1 path every |c| of a
+    tensor is equal, so all codes are +-Qmax and the sign is again sgn(g)."""
+    W, steps = 4, 10
+    sizes = [64, 4096 + 128]
+    wl = wls.Workload(name="cf", tensors=[("a", sizes[0]), ("b", sizes[1])], W=W, agg=agg,
+                      qbits=4 if agg == "l1" else 0)
+    d, ld = wl.d, wl.ld
+    rs = np.random.default_rng(3)
+    mag = np.where(np.arange(d) < sizes[0], 1e-3, 3e-2)      # equal |g| per tensor
+    gv = (mag * np.where(rs.random(d) < 0.5, -1.0, 1.0)).astype(np.float32)
+    theta0 = rs.normal(0, 0.02, d).astype(np.float32)
+    theta0[:4] = [0.02, -0.02, 0.0, 5.0]
+    theta = theta0.copy()
+    m = np.zeros((W, ld), np.float32)
+    g = np.zeros((W, ld), np.float32)
+    g[:, :d] = gv
+    _run(oracle, wl, theta, m, lambda t: g, steps)
+    lr, wd, b2 = float(np.float32(wl.lr)), float(np.float32(wl.wd)), float(np.float32(wl.beta2))
+    a = 1.0 - lr * wd
+    s = np.sign(gv.astype(np.float64))
+    th_cf = a**steps * theta0.astype(np.float64) - s * (1 - a**steps) / wd
+    m_cf = (1 - b2**steps) * gv.astype(np.float64)
+    np.testing.assert_allclose(theta, th_cf, rtol=2e-6, atol=1e-9)
+    for i in range(W):
+        np.testing.assert_allclose(m[i, :d], m_cf, rtol=2e-6)
+    # the worked value theta_0 = 0.02, g > 0 after 10 steps of these hyperparameters
+    if gv[0] > 0:
+        assert abs(theta[0] - 0.0189980450888024) < 1e-8
+
+
+def test_vote_single_worker_is_lion(oracle):
+    """W = 1: the majority vote of one worker is that worker's sign, so the
+    step is plain Lion on c = b1 m + (1-b1) g (no ties for odd W)."""
+    wl = one_tensor(128, 1)
+    rs = np.random.default_rng(5)
+    theta = rs.normal(0, 0.02, 128).astype(np.float32)
+    m = np.zeros((1, 128), np.float32)
+    m[0] = rs.normal(0, 1e-3, 128).astype(np.float32)
+    g = rs.standard_t(3, (1, 128)).astype(np.float32) * np.float32(1e-3)
+    c = np.float32(0.9) * m[0] + np.float32(np.float32(1) - np.float32(0.9)) * g[0]
+    dbg = oracle.step(wl, theta, m, g, 1, debug=True)
+    assert np.array_equal(dbg["sign"], np.where(c > 0, 1, -1).astype(np.int8))
+
+
+def test_sign_flip_step_closed_form(oracle):
+    """Single worker, m_0 = 1, constant g = -0.05.  The momentum follows
+    m_t = b2^t (m_0 - g) + g, so c_t = b1 b2^(t-1) (m_0 - g) + g changes sign
+    at the first t with b2^(t-1) < -g / (b1 (m_0 - g)).  Before that step the
+    update is -lr, after it +lr (plus decay); theta has the geometric-sum
+    closed form.  A swapped b1/b2, a swapped (1-b) factor, or a sign error in
+    either update moves the flip step or the limits."""
+    b1, b2, m0, gval, steps = 0.9, 0.99, 1.0, -0.05, 400
+    wl = one_tensor(64, 1, beta1=b1, beta2=b2)
+    theta = np.full(64, 0.5, np.float32)
+    m = np.full((1, 64), m0, np.float32)
+    g = np.full((1, 64), gval, np.float32)
+    signs = [int(dbg["sign"][0]) for dbg in _run(oracle, wl, theta, m, lambda t: g, steps,
+                                                 debug=True)]
+    ratio = -gval / (b1 * (m0 - gval))
+    t_flip = 1 + math.floor(math.log(ratio) / math.log(b2)) + 1
+    assert signs[: t_flip - 1] == [1] * (t_flip - 1)
+    assert signs[t_flip - 1:] == [-1] * (steps - t_flip + 1)
+    assert t_flip == 294
+    # theta closed form: theta_T = a^T theta_0 - lr * sum_t a^(T-t) s_t
+    lr, wd = float(np.float32(1e-4)), float(np.float32(0.1))
+    a = 1 - lr * wd
+    T = steps
+    k = t_flip - 1                                     # steps with s = +1
+    pos = sum(a ** (T - t) for t in range(1, k + 1))
+    neg = sum(a ** (T - t) for t in range(k + 1, T + 1))
+    th = a**T * 0.5 - lr * (pos - neg)
+    np.testing.assert_allclose(theta, th, rtol=1e-5)
+    mT = b2**T * (m0 - gval) + gval
+    np.testing.assert_allclose(m[0], mT, atol=2e-6)
+
+
+def test_bf16_theta_one_ulp_of_closed_form(oracle):
+    """bf16 parameters: the widened value follows the same closed form to
+    within one bf16 ulp per step (the step is computed in fp32, then rounded
+    once to bf16)."""
+    W = 2
+    wl = one_tensor(256, W, theta_dtype="bf16", grad_dtype="bf16")
+    rs = np.random.default_rng(11)
+    th32 = rs.normal(0, 0.5, 256).astype(np.float32)
+    from synth.gen import to_bf16_bits
+    theta = to_bf16_bits(th32)
+    th0 = bf16_bits_to_f32(theta).astype(np.float64)
+    m = np.zeros((W, 256), np.float32)
+    gv = np.where(rs.random(256) < 0.5, -1e-3, 1e-3).astype(np.float32)
+    g = np.tile(to_bf16_bits(gv), (W, 1))
+    oracle.step(wl, theta, m, g, 1)
+    s = np.sign(gv)
+    lr, wd = float(np.float32(1e-4)), float(np.float32(0.1))
+    want = th0 - lr * (s + wd * th0)
+    got = bf16_bits_to_f32(theta).astype(np.float64)
+    ulp = 2.0 ** (np.floor(np.log2(np.abs(want))) - 7)
+    assert np.all(np.abs(got - want) <= ulp * 0.5 + 1e-12)
+
+
+# ------------------------------------------------------ L1 quantisation ----
+
+def _quant_one(oracle, x, n):
+    W = 1
+    x = np.asarray(x, dtype=np.float32)
+    d = x.size
+    wl = one_tensor(d, W, agg="l1", qbits=n)
+    xx = np.zeros((1, wl.ld), np.float32)
+    xx[0, :d] = x
+    codes, m1 = oracle.quant_l1(wl, xx)
+    return codes[0, :d].tolist(), float(m1[0, 0])
+
+
+def test_quant_l1_handworked(oracle):
+    """Eq. (1) worked by hand, including products that land exactly on .5,
+    which pin round-half-to-even against round-half-away."""
+    codes, M = _quant_one(oracle, [0.5, -0.1, 0, 2, -3, 0.25, 0.05, -0.05], 4)
+    assert codes == [5, -1, 0, 7, -7, 2, 0, 0]
+    assert abs(M - 0.743750000372529) < 1e-15
+    codes, M = _quant_one(oracle, [0.5, -0.5, 1.5, -1.5], 2)
+    assert (codes, M) == ([0, 0, 1, -1], 1.0)              # half-away: [1,-1,1,-1]
+    codes, M = _quant_one(oracle, [0.5, 1.5, 2.5, -2.5, 8.0], 3)
+    assert (codes, M) == ([0, 2, 2, -2, 3], 3.0)           # half-away: [1,2,3,-3,3]
+    codes, M = _quant_one(oracle, [0.0, -0.0, 0.0, 0.0], 4)
+    assert (codes, M) == ([0, 0, 0, 0], 0.0)
+
+
+def _nearest_even(y: Fraction) -> int:
+    f = math.floor(y)
+    r = y - f
+    if r > Fraction(1, 2):
+        return f + 1
+    if r < Fraction(1, 2):
+        return f
+    return f if f % 2 == 0 else f + 1
+
+
+@pytest.mark.parametrize("n", [2, 3, 4, 8])
+def test_quant_l1_exact_rational(oracle, n):
+    """Random dyadic rows: M1 is the exact mean |x| (every partial sum is
+    exact), and each code is the integer in [-Qmax, Qmax] nearest to
+    Qmax*x/M1 in exact rational arithmetic, ties to even.  Where the exact
+    value lies within the fp64 rounding of the scale and product (2^-48
+    relative) of a half-integer, either neighbour is accepted."""
+    qmax = 2 ** (n - 1) - 1
+    rs = np.random.default_rng(100 + n)
+    for trial in range(60):
+        L = int(rs.integers(1, 40))
+        ks = rs.integers(-300, 301, L)
+        if trial % 7 == 0:
+            ks[rs.integers(0, L)] = 5000                     # a heavy tail value
+        x = ks.astype(np.float32) / np.float32(64)
+        codes, M = _quant_one(oracle, x, n)
+        S = sum(Fraction(int(abs(k)), 64) for k in ks)
+        Mx = S / L
+        assert M == float(Mx) or (S == 0 and M == 0.0)
+        for xv, k, q in zip(x, ks, codes):
+            if S == 0:
+                assert q == 0
+                continue
+            y = Fraction(int(k), 64) * qmax / Mx
+            want = max(-qmax, min(qmax, _nearest_even(y)))
+            if want != q:
+                frac = y - math.floor(y)
+                near_half = abs(frac - Fraction(1, 2)) <= abs(y) * Fraction(1, 2**48)
+                assert near_half and abs(q - want) == 1 and abs(q) <= qmax, (x, y, q, want)
+
+
+def test_quant_l1_invariants(oracle):
+    """Q1(2^k x) = Q1(x) (M1 scales with x) and Q1(-x) = -Q1(x)."""
+    rs = np.random.default_rng(9)
+    x = (rs.standard_t(3, 5000) * 1e-3).astype(np.float32)
+    for n in (2, 4, 8):
+        base, _ = _quant_one(oracle, x, n)
+        for k in (-5, -1, 1, 7):
+            sc, _ = _quant_one(oracle, x * np.float32(2.0**k), n)
+            assert sc == base
+        neg, _ = _quant_one(oracle, -x, n)
+        assert neg == [-v for v in base]
+
+
+# ------------------------------------------------------------- mean |x| ---
+
+@pytest.mark.parametrize("n", [1, 63, 64, 4095, 4096, 4097, 3 * 4096 + 896,
+                               70 * 4096 + 13 * 64, 131 * 4096])
+def test_m1_exact_when_sums_are_exact(oracle, n):
+    """Values on a 2^-10 grid in [-4, 4]: every partial sum is exact in fp64
+    whatever the order, so M1 must be the exact mean rounded once (Python's
+    Fraction -> float is correctly rounded).  Spans ragged blocks and more
+    than 64 blocks (several partials per finalize lane)."""
+    rs = np.random.default_rng(n)
+    k = rs.integers(-4096, 4097, n)
+    x = (k.astype(np.float64) / 1024).astype(np.float32)
+    got = oracle.m1(x)
+    want = float(Fraction(int(np.abs(k).sum()), 1024 * n))
+    assert got == want
+
+
+@pytest.mark.parametrize("n", [4096, 70 * 4096 + 13 * 64])
+def test_m1_within_summation_error_bound(oracle, n):
+    """Magnitudes spread over 1e-30..1e30: the fixed-order tree must lie
+    within the worst-case bound of its depth from the correctly rounded sum
+    (math.fsum), so no element is dropped, doubled or misindexed."""
+    rs = np.random.default_rng(n + 1)
+    x = (10.0 ** rs.uniform(-30, 30, n) * np.where(rs.random(n) < 0.5, -1, 1)).astype(np.float32)
+    exact = math.fsum(np.abs(x.astype(np.float64)).tolist())
+    nb = (n + 4095) // 4096
+    depth = 2 + 4 + 6 + 2 + (nb + 63) // 64 + 6 + 1
+    bound = depth * 2.0**-53 * exact * 1.01
+    got = oracle.m1(x) * n
+    assert abs(got - exact) <= bound
+    # dropping one element must violate the bound for the largest element
+    j = int(np.argmax(np.abs(x)))
+    y = x.copy()
+    y[j] = 0
+    assert abs(oracle.m1(y) * n - exact) > bound
+
+
+def test_m1_block_reads_past_n_as_zero(oracle):
+    rs = np.random.default_rng(2)
+    for n in (1, 5, 1000, 4095):
+        a = rs.standard_normal(n).astype(np.float32)
+        pad = np.zeros(4096, np.float32)
+        pad[:n] = a
+        assert oracle.m1_block(a) == oracle.m1_block(pad)
+
+
+# ------------------------------------------------ integer sum and sign ----
+
+def test_l1_sum_handworked(oracle):
+    """W=2, n=2, one 4-element tensor.  With b1 = 0.5 and m = 0, c = g/2
+    exactly and Q1 is scale-free, so the codes are those of g:
+      w0 = [0.5, -0.5, 1.5, -1.5]: M1 = 1, codes [0, 0, 1, -1]
+      w1 = [1, -3, -1, 1]:        M1 = 1.5, codes [1, -1, -1, 1]
+    S = [1, -1, 0, 0] -> sign [+1, -1, 0, 0]; a zero sign only decays theta."""
+    wl = one_tensor(4, 2, agg="l1", qbits=2, beta1=0.5)
+    theta = np.array([0.02, 0.02, 0.02, -0.3], np.float32)
+    th0 = theta.copy()
+    m = np.zeros((2, 64), np.float32)
+    g = np.zeros((2, 64), np.float32)
+    g[0, :4] = [0.5, -0.5, 1.5, -1.5]
+    g[1, :4] = [1, -3, -1, 1]
+    dbg = oracle.step(wl, theta, m, g, 1, debug=True)
+    assert dbg["codes"][0, :4].tolist() == [0, 0, 1, -1]
+    assert dbg["codes"][1, :4].tolist() == [1, -1, -1, 1]
+    assert dbg["sums"].tolist() == [1, -1, 0, 0]
+    assert dbg["sign"].tolist() == [1, -1, 0, 0]
+    a = 1 - float(np.float32(1e-4)) * float(np.float32(0.1))
+    np.testing.assert_allclose(theta[2:], a * th0[2:].astype(np.float64), rtol=1e-7)
+    assert theta[0] < th0[0] - 9e-5 and theta[1] > th0[1] + 9e-5
+
+
+def test_l1_sums_are_column_sums_of_codes(oracle):
+    wl = wls.Workload(name="s", tensors=[("a", 4096 * 2 + 64), ("b", 192)], W=5, agg="l1",
+                      qbits=3)
+    rs = np.random.default_rng(4)
+    theta = rs.normal(0, 0.02, wl.d).astype(np.float32)
+    m = rs.normal(0, 1e-3, (wl.W, wl.ld)).astype(np.float32)
+    g = (rs.standard_t(2.5, (wl.W, wl.ld)) * 1e-3).astype(np.float32)
+    dbg = oracle.step(wl, theta, m, g, 1, debug=True)
+    S = dbg["codes"][:, : wl.d].astype(np.int32).sum(axis=0)
+    assert np.array_equal(S, dbg["sums"])
+    assert np.array_equal(np.sign(S).astype(np.int8), dbg["sign"])
+    assert np.abs(dbg["codes"]).max() <= 3
+
+
+# --------------------------------------------------- momentum averaging ---
+
+def test_selective_momentum_average(oracle):
+    """b2 = 0.5 and small integers make every momentum exact; on averaging
+    steps the flagged tensor's rows all equal the exact worker mean, the
+    other tensor is untouched relative to a run without averaging, and
+    averaging happens only on steps t % sync_every == 0."""
+    W = 4
+    base = wls.Workload(name="sync", tensors=[("wte", 128), ("h0", 64)], W=W, beta2=0.5,
+                        sync_names=("wte",), sync_every=3)
+    nosync = base.with_(sync_names=())
+    rs = np.random.default_rng(8)
+    m0 = rs.integers(-8, 9, (W, base.ld)).astype(np.float32)
+    gs = [rs.integers(-8, 9, (W, base.ld)).astype(np.float32) for _ in range(6)]
+    th = np.zeros(base.d, np.float32)
+    mA, mB = m0.copy(), m0.copy()
+    thA, thB = th.copy(), th.copy()
+    mexact = [[Fraction(int(v)) for v in row] for row in m0[:, :base.d]]
+    for t in range(1, 7):
+        oracle.step(base, thA, mA, gs[t - 1], t)
+        oracle.step(nosync, thB, mB, gs[t - 1], t)
+        for i in range(W):
+            for j in range(base.d):
+                mexact[i][j] = mexact[i][j] / 2 + Fraction(int(gs[t - 1][i, j])) / 2
+        if t % 3 == 0:
+            for j in range(128):
+                avg = sum(mexact[i][j] for i in range(W)) / W
+                for i in range(W):
+                    mexact[i][j] = avg
+        for i in range(W):
+            assert [Fraction(float(v)) for v in mA[i, :base.d]] == mexact[i]
+        assert np.array_equal(mA[:, 128:base.d], mB[:, 128:base.d])
+        if t % 3 == 0:
+            assert np.all(mA[:, :128] == mA[0, :128])
+        if t < 3:                      # no averaging yet: identical runs
+            assert np.array_equal(mA, mB) and np.array_equal(thA, thB)
+
+
+# --------------------------------------------- tie rate (statistical) -----
+
+@pytest.mark.parametrize("W", [4, 8, 16])
+def test_majority_tie_rate(oracle, W):
+    """Lion Cub page (reference note on majority voting): with 4 workers over
+    30% of votes tie, fewer with 8.  For iid symmetric c the tie rate is
+    C(W, W/2) / 2^W (0.375, 0.273, 0.196); the oracle's counts must match it
+    within 5 sigma."""
+    d = 1 << 16
+    wl = one_tensor(d, W)
+    rs = np.random.default_rng(W)
+    theta = np.zeros(d, np.float32)
+    m = rs.normal(0, 1e-3, (W, d)).astype(np.float32)
+    g = (rs.standard_t(3, (W, d)) * 1e-3).astype(np.float32)
+    dbg = oracle.step(wl, theta, m, g, 1, debug=True)
+    p = math.comb(W, W // 2) / 2**W
+    rate = float(np.mean(2 * dbg["counts"].astype(int) == W))
+    assert abs(rate - p) < 5 * math.sqrt(p * (1 - p) / d)
+    if W == 4:
+        assert rate > 0.30
+
+
+# ------------------------------------------------- streaming form ---------
+
+@pytest.mark.parametrize("agg", ["vote", "l1"])
+def test_chunked_step_equals_whole_step(oracle, agg):
+    wl = wls.Workload(name="chunk", tensors=[("a", 4096 * 3 + 640), ("b", 64), ("c", 8192)],
+                      W=3, agg=agg, qbits=4 if agg == "l1" else 0, sync_names=("b",),
+                      grad_dtype="bf16", theta_dtype="bf16")
+    from synth import gen
+    theta = gen.host_theta(wl)
+    m = gen.host_m(wl)
+    g = gen.host_g(wl, 1)
+    th1, m_1 = theta.copy(), m.copy()
+    oracle.step(wl, th1, m_1, g, 2)
+    m1v = oracle.m1_all(wl, m, g) if agg == "l1" else None
+    th2, m_2 = theta.copy(), m.copy()
+    edges = [0, 4096, 4096 * 3, wl.offsets[1] + 64, wl.d]
+    for j0, j1 in zip(edges[:-1], edges[1:]):
+        tc = np.ascontiguousarray(th2[j0:j1])
+        mc = np.ascontiguousarray(m_2[:, j0:j1])
+        gc = np.ascontiguousarray(g[:, j0:j1])
+        oracle.step_range(wl, j0, j1, m1v, tc, mc, gc, 2)
+        th2[j0:j1] = tc
+        m_2[:, j0:j1] = mc
+    assert np.array_equal(th1, th2)
+    assert np.array_equal(m_1, m_2)
