@@ -1,0 +1,77 @@
+"""MI355X (gfx950) Lion Cub / Distributed Lion compressed-update step.
+
+The library (liblioncub.so, C ABI in include/lioncub.h) runs W simulated
+data-parallel workers stacked in one GPU's memory: each forms its Lion update
+vector, compresses it to a 0/1 sign bitmap or to L1-quantised n-bit codes,
+the workers are aggregated by majority vote or integer sum, and the global
+sign updates the parameters and each worker's momentum.  `_abi` mirrors the C
+entry points; `LionCub` keeps a context and its workspace together.
+"""
+from . import _abi
+from ._abi import (AGG_L1SUM, AGG_VOTE, BF16, F32, TIE_PARITY, TIE_ZERO, LionCubError,
+                   lioncub_destroy, lioncub_init, lioncub_pack, lioncub_profile_begin,
+                   lioncub_profile_end, lioncub_quant_l1, lioncub_set_stream, lioncub_step,
+                   lioncub_strerror, lioncub_vote, lioncub_workspace_bytes, make_config)
+
+__all__ = ["LionCub", "LionCubError", "make_config", "lioncub_workspace_bytes", "lioncub_init",
+           "lioncub_set_stream", "lioncub_step", "lioncub_pack", "lioncub_vote",
+           "lioncub_quant_l1", "lioncub_profile_begin", "lioncub_profile_end",
+           "lioncub_destroy", "lioncub_strerror", "F32", "BF16", "AGG_VOTE", "AGG_L1SUM",
+           "TIE_PARITY", "TIE_ZERO"]
+
+
+class LionCub:
+    """One context: configuration, a torch-allocated workspace, a stream.
+
+    theta: [d] fp32/bf16, m: [W][ld] fp32, g: [W][ld] fp32/bf16, all torch
+    tensors on the device; updated in place by step()."""
+
+    def __init__(self, d, W, tensor_offsets=None, ld=None, sync_m=None, sync_every=1,
+                 theta_dtype="f32", grad_dtype="f32", agg="vote", qbits=0, tie="parity",
+                 beta1=0.9, beta2=0.99, lr=1e-4, wd=0.1, device="cuda", stream=None):
+        import torch
+        ld = ld if ld is not None else (d + 63) // 64 * 64
+        offs = tensor_offsets if tensor_offsets is not None else [0, d]
+        self.cfg = make_config(
+            d, ld, W, offs, sync_m=sync_m, sync_every=sync_every,
+            theta_dtype=BF16 if theta_dtype == "bf16" else F32,
+            grad_dtype=BF16 if grad_dtype == "bf16" else F32,
+            agg=AGG_L1SUM if agg == "l1" else AGG_VOTE, qbits=qbits,
+            tie_mode=TIE_ZERO if tie == "zero" else TIE_PARITY,
+            beta1=beta1, beta2=beta2, lr=lr, wd=wd)
+        self.d, self.ld, self.W, self.n_tensors = d, ld, W, len(offs) - 1
+        nbytes = lioncub_workspace_bytes(self.cfg)
+        if nbytes == 0:
+            raise LionCubError("lioncub_workspace_bytes", _abi.EINVAL)
+        self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        self.stream = stream if stream is not None else torch.cuda.current_stream(device)
+        self.ctx = lioncub_init(self.cfg, _abi._stream_handle(self.stream), self.workspace)
+
+    def step(self, theta, m, g, t, debug=None):
+        lioncub_step(self.ctx, theta, m, g, t, debug)
+
+    def pack(self, x, t, bits):
+        lioncub_pack(self.ctx, x, t, bits)
+
+    def vote(self, bits, t, counts=None, sign=None):
+        lioncub_vote(self.ctx, bits, t, counts, sign)
+
+    def quant_l1(self, x, codes, m1=None):
+        lioncub_quant_l1(self.ctx, x, codes, m1)
+
+    def profile_begin(self, capacity):
+        lioncub_profile_begin(self.ctx, capacity)
+
+    def profile_end(self):
+        return lioncub_profile_end(self.ctx)
+
+    def close(self):
+        if getattr(self, "ctx", None) is not None:
+            lioncub_destroy(self.ctx)
+            self.ctx = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -1,0 +1,154 @@
+// device.hpp -- gfx950 device helpers: quad loads/stores, bf16, bit tricks.
+//
+// All floating point here is one IEEE operation at a time (the translation
+// units are built with -ffp-contract=off and carry the pragma below).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#pragma clang fp contract(off)
+
+namespace lioncub {
+
+// ---------------------------------------------------------------- bf16 ----
+
+__device__ __forceinline__ float bf16_widen(uint32_t h) {
+  return __uint_as_float(h << 16);
+}
+
+// fp32 -> bf16, round to nearest even on the 16 dropped bits; NaN -> 0x7FC0.
+__device__ __forceinline__ uint32_t bf16_narrow(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// --------------------------------------------------------- quad loads ----
+// A "quad" is 4 consecutive elements owned by one thread.  nv (0..4) is the
+// number that exist; the rest read as 0 and are never stored.  nv == 4 takes
+// one vector access (16 bytes fp32, 8 bytes bf16).
+
+struct F4 { float v[4]; };
+
+__device__ __forceinline__ F4 ld_f32x4(const float* __restrict__ p, int nv) {
+  F4 r;
+  if (nv == 4) {
+    float4 q = *reinterpret_cast<const float4*>(p);
+    r.v[0] = q.x; r.v[1] = q.y; r.v[2] = q.z; r.v[3] = q.w;
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) r.v[k] = k < nv ? p[k] : 0.0f;
+  }
+  return r;
+}
+
+__device__ __forceinline__ F4 ld_bf16x4(const uint16_t* __restrict__ p, int nv) {
+  F4 r;
+  if (nv == 4) {
+    uint2 q = *reinterpret_cast<const uint2*>(p);
+    r.v[0] = bf16_widen(q.x & 0xFFFFu); r.v[1] = bf16_widen(q.x >> 16);
+    r.v[2] = bf16_widen(q.y & 0xFFFFu); r.v[3] = bf16_widen(q.y >> 16);
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) r.v[k] = k < nv ? bf16_widen(p[k]) : 0.0f;
+  }
+  return r;
+}
+
+template <int BF16>
+__device__ __forceinline__ F4 ld_x4(const void* __restrict__ base, int64_t idx, int nv) {
+  if (BF16) return ld_bf16x4(static_cast<const uint16_t*>(base) + idx, nv);
+  return ld_f32x4(static_cast<const float*>(base) + idx, nv);
+}
+
+__device__ __forceinline__ void st_f32x4(float* __restrict__ p, const F4& a, int nv) {
+  if (nv == 4) {
+    *reinterpret_cast<float4*>(p) = make_float4(a.v[0], a.v[1], a.v[2], a.v[3]);
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      if (k < nv) p[k] = a.v[k];
+  }
+}
+
+__device__ __forceinline__ void st_bf16x4(uint16_t* __restrict__ p, const F4& a, int nv) {
+  if (nv == 4) {
+    uint2 q;
+    q.x = bf16_narrow(a.v[0]) | (bf16_narrow(a.v[1]) << 16);
+    q.y = bf16_narrow(a.v[2]) | (bf16_narrow(a.v[3]) << 16);
+    *reinterpret_cast<uint2*>(p) = q;
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      if (k < nv) p[k] = static_cast<uint16_t>(bf16_narrow(a.v[k]));
+  }
+}
+
+template <int BF16>
+__device__ __forceinline__ void st_x4(void* __restrict__ base, int64_t idx, const F4& a, int nv) {
+  if (BF16) st_bf16x4(static_cast<uint16_t*>(base) + idx, a, nv);
+  else st_f32x4(static_cast<float*>(base) + idx, a, nv);
+}
+
+// Four bytes (one per element) as one 32-bit store when the quad is whole.
+__device__ __forceinline__ void st_b4(void* __restrict__ p, uint32_t packed, int nv) {
+  if (nv == 4) {
+    *reinterpret_cast<uint32_t*>(p) = packed;
+  } else {
+    uint8_t* b = static_cast<uint8_t*>(p);
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      if (k < nv) b[k] = static_cast<uint8_t>(packed >> (8 * k));
+  }
+}
+
+__device__ __forceinline__ void st_i32x4(int32_t* __restrict__ p, const int (&s)[4], int nv) {
+  if (nv == 4) {
+    *reinterpret_cast<int4*>(p) = make_int4(s[0], s[1], s[2], s[3]);
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      if (k < nv) p[k] = s[k];
+  }
+}
+
+// ------------------------------------------------------------ bit tricks --
+
+// Bit k of a 4-bit nibble -> bit 0 of byte k (the four partial products of
+// the multiply land in disjoint bit ranges, so no carries mix them).
+__device__ __forceinline__ uint32_t nibble_to_bytes(uint32_t nib) {
+  return (nib * 0x00204081u) & 0x01010101u;
+}
+
+// Spread the 16 low bits of x so that bit i lands on bit 4*i (Morton-style
+// interleave by masks; "Bit Twiddling Hacks", S. E. Anderson, public domain).
+__device__ __forceinline__ uint64_t spread4(uint64_t x) {
+  x &= 0xFFFFull;
+  x = (x | (x << 24)) & 0x000000FF000000FFull;
+  x = (x | (x << 12)) & 0x000F000F000F000Full;
+  x = (x | (x << 6)) & 0x0303030303030303ull;
+  x = (x | (x << 3)) & 0x1111111111111111ull;
+  return x;
+}
+
+// Wave64 sign bitmap of the 256 consecutive elements held 4 per lane: lane l
+// holds bits nib (bit r = element 4l+r).  Returns, in lanes with l % 16 == 0,
+// the 64-bit word of elements 64*(l/16) .. +63 (LSB first).  Every lane of
+// the wave must call it (inactive lanes contribute zero bits).
+__device__ __forceinline__ uint64_t wave_pack_words(uint32_t nib) {
+  const uint64_t b0 = __ballot(nib & 1u);
+  const uint64_t b1 = __ballot(nib & 2u);
+  const uint64_t b2 = __ballot(nib & 4u);
+  const uint64_t b3 = __ballot(nib & 8u);
+  const int sh = 16 * ((threadIdx.x & 63) >> 4);
+  return spread4(b0 >> sh) | (spread4(b1 >> sh) << 1) | (spread4(b2 >> sh) << 2) |
+         (spread4(b3 >> sh) << 3);
+}
+
+// Sign bit of one element: 1 for c > 0, 0 for c < 0, parity for an exact
+// zero (and for anything unordered).
+__device__ __forceinline__ uint32_t sign_bit(float c, uint32_t parity) {
+  return c > 0.0f ? 1u : (c < 0.0f ? 0u : parity);
+}
+
+}  // namespace lioncub

@@ -1,0 +1,74 @@
+// layout.hpp -- host/device shared tables and kernel parameter blocks.
+//
+// The flat parameter vector is cut into tensors (offsets multiples of 64) and
+// every tensor into blocks of kBlock elements; a block never straddles a
+// tensor, so a workgroup sees one tensor's flags and scales.  The tables live
+// in the caller's workspace, uploaded once at init.
+#pragma once
+#include <stdint.h>
+
+namespace lioncub {
+
+constexpr int kBlock = 4096;    // elements per block (and per mean-|x| partial)
+constexpr int kThreads = 256;   // threads per workgroup (4 wave64)
+constexpr int kQuad = 4;        // consecutive elements per thread and round
+constexpr int kRounds = kBlock / (kThreads * kQuad);  // 4
+constexpr int kWave = 64;
+
+struct BlockEnt {      // 16 bytes
+  int64_t start;       // first element (global index)
+  int32_t len;         // 1..kBlock
+  int32_t tensor;
+};
+
+struct TensorEnt {     // 32 bytes
+  int64_t off;         // first element
+  int64_t n;           // elements
+  int32_t blk0;        // first block id
+  int32_t nblk;        // blocks
+  int32_t sync;        // momentum averaged over workers on averaging steps
+  int32_t pad;
+};
+
+struct StepParams {
+  const BlockEnt* blk;
+  const TensorEnt* tens;
+  void* theta;         // [d] fp32 or bf16
+  float* m;            // [W][ld]
+  const void* g;       // [W][ld] fp32 or bf16
+  const double* scale; // [W][nT] (L1 path): Qmax / M1, 0 when M1 == 0
+  int64_t ld;
+  int32_t W;
+  int32_t nT;
+  float beta1, omega1, beta2, omega2, lr, wd;
+  int32_t parity;      // t & 1
+  int32_t avg_step;    // t % sync_every == 0
+  int32_t tie_zero;
+  int32_t qmax;
+  // optional outputs
+  uint64_t* bits;
+  int8_t* codes;
+  uint8_t* counts;
+  int32_t* sums;
+  int8_t* sign;
+};
+
+struct M1Params {
+  const BlockEnt* blk;
+  const TensorEnt* tens;
+  const float* x;      // [W][ld] source c (quant_l1), or
+  const float* m;      // [W][ld] with
+  const void* g;       // [W][ld]: c = beta1*m + omega1*g
+  double* partial;     // [W][nblk]
+  double* m1;          // [W][nT]
+  double* scale;       // [W][nT]
+  double* m1_out;      // optional caller copy of m1 [W][nT]
+  int64_t ld;
+  int32_t W;
+  int32_t nT;
+  int32_t nblk;
+  int32_t qmax;
+  float beta1, omega1;
+};
+
+}  // namespace lioncub

@@ -1,0 +1,234 @@
+// step.hip -- fused Lion Cub step kernels for gfx950.
+//
+// One workgroup (256 threads, 4 wave64) per block of 4096 elements of one
+// tensor; each thread owns one quad (4 consecutive elements) per round, 4
+// rounds.  For its quad a thread walks the W workers: loads m_i and g_i
+// (coalesced 16-byte / 8-byte vector loads), forms c_i = beta1*m_i +
+// omega1*g_i, compresses it (sign bit, or Eq. (1) code), accumulates the
+// aggregate (vote count, or integer sum) and immediately writes the new
+// momentum m_i' = beta2*m_i + omega2*g_i -- m_i' does not depend on the
+// global sign, so each worker's state is touched exactly once.  After the
+// last worker it applies the global sign to theta.  On averaging steps of a
+// designated tensor the new momenta are summed in worker order instead and
+// their mean is written to every worker.
+//
+// Method: "Lion Cub: Minimizing Communication Overhead in Distributed Lion"
+// (pith.science review, "What carries the argument": c_{i,t}, 0/1 packing
+// with parity zeros, Eq. (1), the quantised sum and global sign; selective
+// momentum synchronisation of the embedding and output layers), and the
+// D-Lion summary page ("Approach": per-worker momentum, majority vote).
+//
+// Workers are processed in batches of WB: all 2*WB loads of a batch are
+// issued before any use, which gives every wave 2*WB outstanding vector
+// loads; the batch's momentum stores follow.  HBM-bound: per element it moves
+// W*(4 + s_g + 4) + 2*s_theta bytes (vote) -- nothing else.
+#include "device.hpp"
+#include "layout.hpp"
+
+#pragma clang fp contract(off)
+
+namespace lioncub {
+
+// One round of one thread: its quad at element j (nv of 4 valid), all
+// workers.  FULL rounds (every lane of the workgroup has a whole quad) take
+// straight vector loads with no per-lane predicates; WT > 0 fixes W at compile
+// time so the worker loop has no bounds tests.
+template <int TT, int GT, bool DBG, int AGG, int WB, int WT, bool FULL>
+__device__ __forceinline__ void step_round(const StepParams& p, int tensor, int64_t j, int nv,
+                                           bool avg, uint32_t par) {
+  const int W = WT > 0 ? WT : p.W;
+  if (FULL) nv = kQuad;
+  const int tid = threadIdx.x;
+  const double* __restrict__ scl = p.scale + tensor;  // scl[i*nT]
+  float* __restrict__ m = p.m;
+
+  // theta does not change until the end of the round: fetch it first
+  F4 th;
+  if (FULL || nv > 0) th = ld_x4<TT>(p.theta, j, nv);
+
+  uint32_t cnt = 0;           // vote: per-element counts, one byte each
+  int sum[4] = {0, 0, 0, 0};  // L1: per-element integer sums
+  F4 acc;                     // averaging: running sum of new momenta
+
+#pragma unroll 1
+  for (int i0 = 0; i0 < W; i0 += WB) {
+    F4 mv[WB], gv[WB];
+#pragma unroll
+    for (int b = 0; b < WB; ++b) {
+      if ((WT > 0 && WT % WB == 0) || i0 + b < W) {
+        if (FULL || nv > 0) {
+          const int64_t idx = static_cast<int64_t>(i0 + b) * p.ld + j;
+          mv[b] = ld_f32x4(m + idx, nv);
+          gv[b] = ld_x4<GT>(p.g, idx, nv);
+          continue;
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) mv[b].v[k] = gv[b].v[k] = 0.0f;
+    }
+#pragma unroll
+    for (int b = 0; b < WB; ++b) {
+      const int i = i0 + b;
+      if (!(WT > 0 && WT % WB == 0) && i >= W) break;
+      const int64_t idx = static_cast<int64_t>(i) * p.ld + j;
+      F4 mn;
+      uint32_t nib = 0;
+      double s_i = 0.0;
+      if (AGG == 1) s_i = scl[static_cast<int64_t>(i) * p.nT];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float c = (p.beta1 * mv[b].v[k]) + (p.omega1 * gv[b].v[k]);
+        if (AGG == 0) {
+          nib |= ((FULL || k < nv) ? sign_bit(c, par) : 0u) << k;
+        } else {
+          double y = __builtin_rint(static_cast<double>(c) * s_i);
+          y = fmin(fmax(y, -static_cast<double>(p.qmax)), static_cast<double>(p.qmax));
+          const int q = static_cast<int>(y);
+          sum[k] += q;
+          if (DBG) nib |= (static_cast<uint32_t>(q) & 0xFFu) << (8 * k);
+        }
+        mn.v[k] = (p.beta2 * mv[b].v[k]) + (p.omega2 * gv[b].v[k]);
+      }
+      if (AGG == 0) {
+        cnt += nibble_to_bytes(nib);
+        if (DBG && p.bits) {
+          const uint64_t word = wave_pack_words(nib);
+          if ((tid & 15) == 0 && (FULL || nv > 0))
+            p.bits[static_cast<int64_t>(i) * (p.ld >> 6) + (j >> 6)] = word;
+        }
+      } else if (DBG && p.codes && (FULL || nv > 0)) {
+        st_b4(p.codes + idx, nib, nv);
+      }
+      if (FULL || nv > 0) {
+        if (!avg) {
+          st_f32x4(m + idx, mn, nv);
+        } else if (i == 0) {
+          acc = mn;
+        } else {
+#pragma unroll
+          for (int k = 0; k < 4; ++k) acc.v[k] = acc.v[k] + mn.v[k];
+        }
+      }
+    }
+  }
+  if (!FULL && nv == 0) return;
+
+  // global sign
+  int s[4];
+  if (AGG == 0) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int twice = 2 * static_cast<int>((cnt >> (8 * k)) & 0xFFu);
+      s[k] = twice > W ? 1 : (twice < W ? -1 : (p.tie_zero ? 0 : (par ? 1 : -1)));
+    }
+    if (DBG && p.counts) st_b4(p.counts + j, cnt, nv);
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) s[k] = (sum[k] > 0) - (sum[k] < 0);
+    if (DBG && p.sums) st_i32x4(p.sums + j, sum, nv);
+  }
+  if (DBG && p.sign) {
+    const uint32_t packed = (static_cast<uint32_t>(s[0]) & 0xFFu) |
+                            ((static_cast<uint32_t>(s[1]) & 0xFFu) << 8) |
+                            ((static_cast<uint32_t>(s[2]) & 0xFFu) << 16) |
+                            ((static_cast<uint32_t>(s[3]) & 0xFFu) << 24);
+    st_b4(p.sign + j, packed, nv);
+  }
+
+  // theta <- theta - lr*(sign + wd*theta)
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float x = th.v[k];
+    th.v[k] = x - (p.lr * (static_cast<float>(s[k]) + (p.wd * x)));
+  }
+  st_x4<TT>(p.theta, j, th, nv);
+
+  // worker mean of the new momenta on averaging steps
+  if (avg) {
+    const float fw = static_cast<float>(W);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) acc.v[k] = acc.v[k] / fw;
+#pragma unroll 4
+    for (int i = 0; i < W; ++i) st_f32x4(m + static_cast<int64_t>(i) * p.ld + j, acc, nv);
+  }
+}
+
+template <int TT, int GT, bool DBG, int AGG, int WB, int WT>
+__global__ __launch_bounds__(kThreads) void k_step(StepParams p) {
+  const BlockEnt be = p.blk[blockIdx.x];
+  const int tid = threadIdx.x;
+  const bool avg = p.avg_step && p.tens[be.tensor].sync;
+  const uint32_t par = static_cast<uint32_t>(p.parity);
+#pragma unroll 1
+  for (int r = 0; r < kRounds; ++r) {
+    const int base = kThreads * kQuad * r;
+    const int rem = be.len - base;  // uniform over the workgroup
+    const int64_t j = be.start + base + kQuad * tid;
+    if (rem >= kThreads * kQuad) {
+      step_round<TT, GT, DBG, AGG, WB, WT, true>(p, be.tensor, j, kQuad, avg, par);
+    } else if (rem > 0) {
+      const int nv = max(0, min(kQuad, rem - kQuad * tid));
+      if (DBG || nv > 0) step_round<TT, GT, DBG, AGG, WB, 0, false>(p, be.tensor, j, nv, avg, par);
+    }
+  }
+}
+
+// Zero the words of each row that lie wholly past d (debug bitmaps).
+__global__ void k_zero_tail_words(uint64_t* bits, int64_t words, int64_t first, int W) {
+  const int64_t n = words - first;
+  const int64_t k = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (k >= n * W) return;
+  const int64_t i = k / n, w = first + k % n;
+  bits[i * words + w] = 0;
+}
+
+constexpr int kWB = 8;
+
+template <int TT, int GT, bool DBG, int AGG>
+static hipError_t launch_t(const StepParams& p, int nblk, hipStream_t st) {
+  const dim3 g(nblk), b(kThreads);
+  if constexpr (!DBG) {
+    if (p.W == 4) {
+      hipLaunchKernelGGL((k_step<TT, GT, DBG, AGG, 4, 4>), g, b, 0, st, p);
+      return hipGetLastError();
+    }
+    if (p.W == 8) {
+      hipLaunchKernelGGL((k_step<TT, GT, DBG, AGG, kWB, 8>), g, b, 0, st, p);
+      return hipGetLastError();
+    }
+    if (p.W == 16) {
+      hipLaunchKernelGGL((k_step<TT, GT, DBG, AGG, kWB, 16>), g, b, 0, st, p);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((k_step<TT, GT, DBG, AGG, kWB, 0>), g, b, 0, st, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_step(const StepParams& p, int nblk, int theta_bf16, int grad_bf16, int agg,
+                       hipStream_t st) {
+  const bool dbg = p.bits || p.codes || p.counts || p.sums || p.sign;
+  const int key = (theta_bf16 << 3) | (grad_bf16 << 2) | ((dbg ? 1 : 0) << 1) | agg;
+  switch (key) {
+#define LC_CASE(TT, GT, D, A) \
+  case ((TT << 3) | (GT << 2) | (D << 1) | A): return launch_t<TT, GT, (D != 0), A>(p, nblk, st);
+    LC_CASE(0, 0, 0, 0) LC_CASE(0, 0, 0, 1) LC_CASE(0, 0, 1, 0) LC_CASE(0, 0, 1, 1)
+    LC_CASE(0, 1, 0, 0) LC_CASE(0, 1, 0, 1) LC_CASE(0, 1, 1, 0) LC_CASE(0, 1, 1, 1)
+    LC_CASE(1, 0, 0, 0) LC_CASE(1, 0, 0, 1) LC_CASE(1, 0, 1, 0) LC_CASE(1, 0, 1, 1)
+    LC_CASE(1, 1, 0, 0) LC_CASE(1, 1, 0, 1) LC_CASE(1, 1, 1, 0) LC_CASE(1, 1, 1, 1)
+#undef LC_CASE
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_zero_tail_words(uint64_t* bits, int64_t words, int64_t first, int W,
+                                  hipStream_t st) {
+  const int64_t n = (words - first) * W;
+  if (n <= 0) return hipSuccess;
+  const int64_t grid = (n + 255) / 256;
+  hipLaunchKernelGGL(k_zero_tail_words, dim3(static_cast<unsigned>(grid)), dim3(256), 0, st, bits,
+                     words, first, W);
+  return hipGetLastError();
+}
+
+}  // namespace lioncub

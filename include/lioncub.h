@@ -1,0 +1,181 @@
+/*
+ * lioncub.h -- C ABI of the MI355X (gfx950) Lion Cub compressed-update step.
+ *
+ * The method (sources: "Lion Cub: Minimizing Communication Overhead in
+ * Distributed Lion", pith.science review page, section "What carries the
+ * argument", Eq. (1) and the Figure 1 / Figure 10 captions; "Communication
+ * Efficient Distributed Training with Distributed Lion", atlas.scime.ai
+ * summary, section "Approach"):
+ *
+ *   W data-parallel workers each keep their own momentum m_i and gradient g_i.
+ *   1. every worker forms c_i = beta1*m_i + (1-beta1)*g_i;
+ *   2. c_i is compressed, either to a 0/1 sign bitmap (exact zeros take +1 on
+ *      odd and -1 on even steps) or to n-bit integers by L1 quantisation,
+ *      Q1(x) = clamp(round((2^(n-1)-1) * x / mean|x|), +-(2^(n-1)-1));
+ *   3. the W compressed vectors are aggregated, by majority vote over the
+ *      bitmaps or by an integer sum of the codes;
+ *   4. the global sign is applied: theta <- theta - lr*(sign + wd*theta);
+ *   5. each worker's momentum is updated, m_i <- beta2*m_i + (1-beta2)*g_i,
+ *      and, for designated tensors (the input-embedding and output layers) on
+ *      averaging steps, replaced by the worker mean.
+ *
+ * Here the W workers are stacked buffers in one GPU's memory and the
+ * aggregation is a local kernel.
+ *
+ * Conventions for every entry point:
+ *  - Buffers named "device" are device pointers owned by the caller; the
+ *    library never allocates, frees or retains them past the call.
+ *  - Every call is asynchronous, enqueued on the stream given at init (or by
+ *    lioncub_set_stream), ordered with other work on that stream; no call
+ *    synchronises the host except lioncub_init, lioncub_destroy and
+ *    lioncub_profile_end.
+ *  - Argument errors are detected before anything is enqueued and returned as
+ *    a negative status; nothing is written then.  A failed launch returns
+ *    LIONCUB_EDEVICE.  Faults inside a kernel surface at the caller's next
+ *    synchronisation of the stream.
+ *  - [W][ld] is worker-major: element j of worker i is at index i*ld + j.
+ *    Rows hold d valid elements; ld >= d is a multiple of 64.
+ *  - Bitmaps are little-endian uint64 words, least-significant bit first:
+ *    element j of worker i is bit j%64 of word i*(ld/64) + j/64.  Bit 1 means
+ *    +1 (c > 0, or c == 0 on an odd step).  Bits at j >= d are 0.
+ *  - Data pointers must be 16-byte aligned; inputs and outputs must not
+ *    overlap.  A context is not thread-safe; many contexts may coexist.
+ *  - Floating point is IEEE round-to-nearest-even, one operation at a time,
+ *    no fused multiply-add contraction, subnormals kept.  bf16 values are
+ *    widened exactly and narrowed round-to-nearest-even.
+ */
+#ifndef LIONCUB_H
+#define LIONCUB_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct lioncub_ctx lioncub_ctx; /* opaque, host memory, owned by the library */
+
+enum {
+  LIONCUB_OK = 0,
+  LIONCUB_EINVAL = -1,       /* bad argument or configuration             */
+  LIONCUB_EALIGN = -2,       /* pointer not aligned as required           */
+  LIONCUB_EWORKSPACE = -3,   /* workspace missing, misaligned or too small */
+  LIONCUB_EDEVICE = -4,      /* HIP runtime / launch failure              */
+  LIONCUB_EUNSUPPORTED = -5  /* valid request this build does not support */
+};
+
+enum { LIONCUB_F32 = 0, LIONCUB_BF16 = 1 };
+enum { LIONCUB_AGG_VOTE = 0, LIONCUB_AGG_L1SUM = 1 };
+enum { LIONCUB_TIE_PARITY = 0, LIONCUB_TIE_ZERO = 1 };
+
+typedef struct {
+  int64_t d;                     /* parameters per worker, >= 1                  */
+  int64_t ld;                    /* row stride of [W][ld] buffers, >= d, % 64 == 0 */
+  int32_t W;                     /* workers, 1..255                              */
+  int32_t n_tensors;             /* tensors in the flat vector, >= 1             */
+  const int64_t *tensor_offsets; /* HOST, n_tensors+1: off[0]=0 < off[1] < ... <
+                                    off[n]=d; off[k] % 64 == 0 for k < n.  Read
+                                    during lioncub_init only.                    */
+  const uint8_t *sync_m;         /* HOST, n_tensors flags (1 = momentum averaged
+                                    over workers on averaging steps) or NULL.
+                                    Read during lioncub_init only.               */
+  int32_t sync_every;            /* >= 1: averaging on steps with t % sync_every == 0 */
+  int32_t theta_dtype;           /* LIONCUB_F32 or LIONCUB_BF16                  */
+  int32_t grad_dtype;            /* LIONCUB_F32 or LIONCUB_BF16; m is always fp32 */
+  int32_t agg;                   /* LIONCUB_AGG_VOTE or LIONCUB_AGG_L1SUM        */
+  int32_t qbits;                 /* n of Eq. (1), 2..8; required for L1SUM and for
+                                    lioncub_quant_l1, else ignored               */
+  int32_t tie_mode;              /* vote ties (2*count == W): LIONCUB_TIE_PARITY
+                                    (+1 odd t, -1 even t) or LIONCUB_TIE_ZERO (0) */
+  float beta1, beta2, lr, wd;    /* finite                                       */
+} lioncub_config;
+
+/* Optional per-element outputs of lioncub_step (each member may be NULL). */
+typedef struct {
+  uint64_t *bits;  /* device [W][ld/64]: the workers' sign bitmaps (vote path)  */
+  int8_t *codes;   /* device [W][ld]: Eq. (1) codes (L1 path); j >= d untouched */
+  uint8_t *counts; /* device [d]: number of +1 bits per element (vote path)     */
+  int32_t *sums;   /* device [d]: integer sum of the codes (L1 path)            */
+  int8_t *sign;    /* device [d]: the global sign applied, in {-1, 0, +1}       */
+} lioncub_debug;
+
+/* Bytes of device workspace lioncub_init needs for cfg (0 if cfg is invalid).
+ * Pure host computation. */
+size_t lioncub_workspace_bytes(const lioncub_config *cfg);
+
+/* Validate cfg, lay out the caller's workspace (device, >= the bytes above,
+ * 256-byte aligned, owned by the caller, must outlive the context and not be
+ * touched by the caller while the context lives) and upload the tensor and
+ * block tables into it on hip_stream (a hipStream_t; NULL = the null stream).
+ * Synchronises that stream once.  On success *out receives a new context. */
+int lioncub_init(lioncub_ctx **out, const lioncub_config *cfg, void *hip_stream,
+                 void *workspace, size_t ws_bytes);
+
+/* Switch the stream later calls enqueue on. */
+int lioncub_set_stream(lioncub_ctx *ctx, void *hip_stream);
+
+/* One compressed-update step, steps 1-5 above, in place.
+ *   theta: device [d], fp32 or bf16 per theta_dtype (read, written)
+ *   m:     device [W][ld] fp32 (read, written; columns j >= d untouched)
+ *   g:     device [W][ld], fp32 or bf16 per grad_dtype (read only)
+ *   t:     1-based step index; decides zero and tie parity and averaging steps
+ *   dbg:   NULL, or optional outputs (bits/counts on the vote path,
+ *          codes/sums on the L1 path, sign on both)
+ * The vote path is one kernel; the L1 path is three (mean |c| block partials,
+ * per-(worker, tensor) mean and scale, then the fused quantise-sum-apply). */
+int lioncub_step(lioncub_ctx *ctx, void *theta, float *m, const void *g, int64_t t,
+                 const lioncub_debug *dbg);
+
+/* Sign packing of x = c directly: bits[W][ld/64] (device) from x[W][ld]
+ * (device fp32), zeros by the parity of t (>= 1).  Every word of every row is
+ * written, words past d with zeros. */
+int lioncub_pack(lioncub_ctx *ctx, const float *x, int64_t t, uint64_t *bits);
+
+/* Majority vote over bits[W][ld/64] (device): counts[d] (device, may be NULL)
+ * = number of 1 bits, sign[d] (device, may be NULL) = +1 if 2*count > W, -1 if
+ * 2*count < W, ties per tie_mode with the parity of t (>= 1).  At least one
+ * output must be given. */
+int lioncub_vote(lioncub_ctx *ctx, const uint64_t *bits, int64_t t, uint8_t *counts,
+                 int8_t *sign);
+
+/* L1 quantisation, Eq. (1), of x = c directly: codes[W][ld] (device int8,
+ * columns j >= d untouched) and, if m1 != NULL, m1[W][n_tensors] (device
+ * fp64) = mean |x| of each (worker, tensor), summed in fp64 in the library's
+ * fixed order (blocks of 4096; within a block 256 lanes x 4 rounds of 4
+ * consecutive values, acc += ((e0+e1)+(e2+e3)); 64-lane halving folds; block
+ * partial (w0+w1)+(w2+w3); lane l of one 64-lane group sums partials l, l+64,
+ * ... then folds), then divided by the tensor's element count.  A tensor
+ * with mean 0 gets all-zero codes.  Needs qbits in 2..8 in the config. */
+int lioncub_quant_l1(lioncub_ctx *ctx, const float *x, int8_t *codes, double *m1);
+
+/* Measurement hook: while enabled, every kernel the context launches is
+ * bracketed by HIP events on its stream (at most `capacity` launches are
+ * recorded).  lioncub_profile_end synchronises on the events, disables the
+ * hook and writes, per kernel kind k (LIONCUB_K_*), the summed duration in
+ * ms_total[k] and the launch count in launches[k] (arrays of
+ * LIONCUB_K_COUNT entries, host memory). */
+enum {
+  LIONCUB_K_VOTE_STEP = 0,
+  LIONCUB_K_M1_PARTIAL = 1,
+  LIONCUB_K_M1_FINALIZE = 2,
+  LIONCUB_K_L1_STEP = 3,
+  LIONCUB_K_PACK = 4,
+  LIONCUB_K_VOTE = 5,
+  LIONCUB_K_QUANT = 6,
+  LIONCUB_K_COUNT = 7
+};
+int lioncub_profile_begin(lioncub_ctx *ctx, int32_t capacity);
+int lioncub_profile_end(lioncub_ctx *ctx, double *ms_total, int32_t *launches);
+
+/* Release the context (host memory).  Synchronises its stream first.  NULL
+ * is accepted. */
+int lioncub_destroy(lioncub_ctx *ctx);
+
+/* Static description of a status code. */
+const char *lioncub_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,101 @@
+"""Host-side checks of the C ABI (no GPU needed): the built library loads,
+exports every entry point include/lioncub.h declares, sizes workspaces, and
+rejects bad configurations and arguments before touching the device."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from communication_compressed_distributed_amd import _abi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    txt = open(os.path.join(ROOT, "include", "lioncub.h")).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(lioncub_[a-z0-9_]+)\s*\(", txt)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = _abi.lib()
+    names = header_functions()
+    assert len(names) >= 11
+    for n in names:
+        assert hasattr(L, n), n
+    assert sorted(names) == sorted(_abi.EXPORTS)
+
+
+def test_strerror_names_every_status():
+    for s in (0, -1, -2, -3, -4, -5):
+        assert _abi.lioncub_strerror(s) != "unknown status"
+    assert _abi.lioncub_strerror(7) == "unknown status"
+
+
+def cfg(**kw):
+    base = dict(d=10000, ld=10048, W=4, tensor_offsets=[0, 4096, 10000])
+    base.update(kw)
+    return _abi.make_config(**base)
+
+
+def test_workspace_bytes_layout():
+    # blocks: ceil(4096/4096) + ceil(5904/4096) = 3; 256-byte aligned pieces
+    c = cfg()
+    n = _abi.lioncub_workspace_bytes(c)
+    blk = 3 * 16
+    tens = 2 * 32
+    part = 4 * 3 * 8
+    m1 = 4 * 2 * 8
+    al = lambda x: (x + 255) // 256 * 256
+    assert n == al(blk) + al(tens) + al(part) + 2 * al(m1)
+    big = cfg(d=1_313_626_112, ld=1_313_626_112, W=8,
+              tensor_offsets=[0, 1_000_000_000 // 64 * 64, 1_313_626_112])
+    assert _abi.lioncub_workspace_bytes(big) > 0
+
+
+@pytest.mark.parametrize("bad", [
+    dict(d=0, ld=64, tensor_offsets=[0, 0]),             # empty
+    dict(ld=10000),                                       # ld not multiple of 64
+    dict(ld=9984),                                        # ld < d
+    dict(W=0), dict(W=256),                               # worker count
+    dict(tensor_offsets=[0, 4000, 10000]),                # interior offset not % 64
+    dict(tensor_offsets=[0, 4096, 9999]),                 # last offset != d
+    dict(tensor_offsets=[0, 4096, 4096, 10000]),          # empty tensor
+    dict(tensor_offsets=[64, 4096, 10000]),               # off[0] != 0
+    dict(sync_every=0),
+    dict(theta_dtype=2), dict(grad_dtype=-1),
+    dict(agg=2), dict(agg=_abi.AGG_L1SUM, qbits=1), dict(agg=_abi.AGG_L1SUM, qbits=9),
+    dict(tie_mode=3),
+    dict(lr=float("nan")), dict(beta1=float("inf")),
+])
+def test_invalid_config_rejected_before_device(bad):
+    c = cfg(**bad)
+    assert _abi.lioncub_workspace_bytes(c) == 0
+    ctx = C.c_void_p()
+    st = _abi.lib().lioncub_init(C.byref(ctx), C.byref(c), None, C.c_void_p(256), 1 << 30)
+    assert st == _abi.EINVAL
+    assert not ctx.value
+
+
+def test_workspace_checked_before_device():
+    c = cfg()
+    n = _abi.lioncub_workspace_bytes(c)
+    L = _abi.lib()
+    ctx = C.c_void_p()
+    assert L.lioncub_init(C.byref(ctx), C.byref(c), None, None, n) == _abi.EWORKSPACE
+    assert L.lioncub_init(C.byref(ctx), C.byref(c), None, C.c_void_p(256), n - 1) == _abi.EWORKSPACE
+    assert L.lioncub_init(C.byref(ctx), C.byref(c), None, C.c_void_p(128), n) == _abi.EWORKSPACE
+    assert L.lioncub_init(None, C.byref(c), None, C.c_void_p(256), n) == _abi.EINVAL
+
+
+def test_null_context_and_arguments_rejected():
+    L = _abi.lib()
+    p = C.c_void_p(4096)
+    assert L.lioncub_step(None, p, p, p, 1, None) == _abi.EINVAL
+    assert L.lioncub_pack(None, p, 1, p) == _abi.EINVAL
+    assert L.lioncub_vote(None, p, 1, p, p) == _abi.EINVAL
+    assert L.lioncub_quant_l1(None, p, p, None) == _abi.EINVAL
+    assert L.lioncub_set_stream(None, None) == _abi.EINVAL
+    assert L.lioncub_profile_begin(None, 4) == _abi.EINVAL
+    assert L.lioncub_destroy(None) == _abi.OK
