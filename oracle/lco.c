@@ -135,14 +135,30 @@ double lco_m1_block(const float *a, int64_t n) {
   return (wv[0] + wv[1]) + (wv[2] + wv[3]);
 }
 
-/* Finalize: lane l (0..63) sums the partials of blocks l, l+64, l+128, ...
- * in increasing order from 0.0, the 64 lane sums are folded as above, and
- * the total is divided by the element count. */
+/* Finalize (three levels, so that no summation chain is long): the block
+ * partials of a tensor, in block order, are cut into groups of 256; a group
+ * value folds its partials like a block (partial l of the group in lane l,
+ * 0.0 past the last block, halving folds per 64 lanes, then (w0 + w1) +
+ * (w2 + w3)); lane l (0..63) sums group values l, l+64, l+128, ... in
+ * increasing order from 0.0; the 64 lane sums are folded by halving; the
+ * total is divided by the element count. */
+static double fold_group(const double *P, int64_t cnt) {
+  double acc[LCO_M1_LANES];
+  for (int l = 0; l < LCO_M1_LANES; l++) acc[l] = l < cnt ? P[l] : 0.0;
+  double wv[4];
+  for (int w = 0; w < 4; w++) wv[w] = fold64(acc + LCO_M1_WAVE * w);
+  return (wv[0] + wv[1]) + (wv[2] + wv[3]);
+}
+
 double lco_m1_finalize(const double *P, int64_t nb, int64_t nT) {
+  int64_t ng = (nb + LCO_M1_LANES - 1) / LCO_M1_LANES;
   double p[LCO_M1_WAVE];
-  for (int l = 0; l < LCO_M1_WAVE; l++) {
-    p[l] = 0.0;
-    for (int64_t b = l; b < nb; b += LCO_M1_WAVE) p[l] = p[l] + P[b];
+  for (int l = 0; l < LCO_M1_WAVE; l++) p[l] = 0.0;
+  for (int64_t g = 0; g < ng; g++) {
+    int64_t cnt = nb - g * LCO_M1_LANES;
+    if (cnt > LCO_M1_LANES) cnt = LCO_M1_LANES;
+    double G = fold_group(P + g * LCO_M1_LANES, cnt);
+    p[g % LCO_M1_WAVE] = p[g % LCO_M1_WAVE] + G;
   }
   return fold64(p) / (double)nT;
 }

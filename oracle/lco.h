@@ -84,7 +84,9 @@ void lco_vote(int32_t W, int64_t d, int64_t ld, const uint64_t *bits,
  * block partial).  Values past n count as +0.0. */
 double lco_m1_block(const float *a, int64_t n);
 
-/* M1 from the nb block partials of one (worker, tensor) of nT elements. */
+/* M1 from the nb block partials of one (worker, tensor) of nT elements:
+ * groups of 256 partials folded like a block, group values summed per lane
+ * (lane l takes groups l, l+64, ...), lanes folded, divided by nT. */
 double lco_m1_finalize(const double *P, int64_t nb, int64_t nT);
 
 /* M1 of one row of n values (block partials + finalize). */

@@ -334,7 +334,7 @@ def test_quant_l1_invariants(oracle):
 # ------------------------------------------------------------- mean |x| ---
 
 @pytest.mark.parametrize("n", [1, 63, 64, 4095, 4096, 4097, 3 * 4096 + 896,
-                               70 * 4096 + 13 * 64, 131 * 4096])
+                               70 * 4096 + 13 * 64, 300 * 4096 + 64, 64 * 256 * 4096 + 4096])
 def test_m1_exact_when_sums_are_exact(oracle, n):
     """Values on a 2^-10 grid in [-4, 4]: every partial sum is exact in fp64
     whatever the order, so M1 must be the exact mean rounded once (Python's
@@ -348,7 +348,7 @@ def test_m1_exact_when_sums_are_exact(oracle, n):
     assert got == want
 
 
-@pytest.mark.parametrize("n", [4096, 70 * 4096 + 13 * 64])
+@pytest.mark.parametrize("n", [4096, 70 * 4096 + 13 * 64, 600 * 4096 + 320])
 def test_m1_within_summation_error_bound(oracle, n):
     """Magnitudes spread over 1e-30..1e30: the fixed-order tree must lie
     within the worst-case bound of its depth from the correctly rounded sum
@@ -357,7 +357,8 @@ def test_m1_within_summation_error_bound(oracle, n):
     x = (10.0 ** rs.uniform(-30, 30, n) * np.where(rs.random(n) < 0.5, -1, 1)).astype(np.float32)
     exact = math.fsum(np.abs(x.astype(np.float64)).tolist())
     nb = (n + 4095) // 4096
-    depth = 2 + 4 + 6 + 2 + (nb + 63) // 64 + 6 + 1
+    ng = (nb + 255) // 256
+    depth = 2 + 4 + 6 + 2 + 6 + 2 + (ng + 63) // 64 + 6 + 1
     bound = depth * 2.0**-53 * exact * 1.01
     got = oracle.m1(x) * n
     assert abs(got - exact) <= bound
