@@ -61,6 +61,35 @@ __device__ __forceinline__ F4 ld_x4(const void* __restrict__ base, int64_t idx, 
   return ld_f32x4(static_cast<const float*>(base) + idx, nv);
 }
 
+// Streaming (nontemporal) variants for data touched once per step: the
+// whole-quad case uses the nontemporal hint, which on gfx950 lifts a pure
+// read stream from ~6.4 to ~7.1 TB/s; partial quads fall back to plain loads.
+typedef float v4f_t __attribute__((ext_vector_type(4)));
+typedef unsigned int v2u_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ F4 ldnt_f32x4(const float* __restrict__ p, int nv) {
+  if (nv != 4) return ld_f32x4(p, nv);
+  const v4f_t q = __builtin_nontemporal_load(reinterpret_cast<const v4f_t*>(p));
+  F4 r;
+  r.v[0] = q.x; r.v[1] = q.y; r.v[2] = q.z; r.v[3] = q.w;
+  return r;
+}
+
+__device__ __forceinline__ F4 ldnt_bf16x4(const uint16_t* __restrict__ p, int nv) {
+  if (nv != 4) return ld_bf16x4(p, nv);
+  const v2u_t q = __builtin_nontemporal_load(reinterpret_cast<const v2u_t*>(p));
+  F4 r;
+  r.v[0] = bf16_widen(q.x & 0xFFFFu); r.v[1] = bf16_widen(q.x >> 16);
+  r.v[2] = bf16_widen(q.y & 0xFFFFu); r.v[3] = bf16_widen(q.y >> 16);
+  return r;
+}
+
+template <int BF16>
+__device__ __forceinline__ F4 ldnt_x4(const void* __restrict__ base, int64_t idx, int nv) {
+  if (BF16) return ldnt_bf16x4(static_cast<const uint16_t*>(base) + idx, nv);
+  return ldnt_f32x4(static_cast<const float*>(base) + idx, nv);
+}
+
 __device__ __forceinline__ void st_f32x4(float* __restrict__ p, const F4& a, int nv) {
   if (nv == 4) {
     *reinterpret_cast<float4*>(p) = make_float4(a.v[0], a.v[1], a.v[2], a.v[3]);
@@ -82,6 +111,15 @@ __device__ __forceinline__ void st_bf16x4(uint16_t* __restrict__ p, const F4& a,
     for (int k = 0; k < 4; ++k)
       if (k < nv) p[k] = static_cast<uint16_t>(bf16_narrow(a.v[k]));
   }
+}
+
+__device__ __forceinline__ void stnt_f32x4(float* __restrict__ p, const F4& a, int nv) {
+  if (nv != 4) {
+    st_f32x4(p, a, nv);
+    return;
+  }
+  const v4f_t q = {a.v[0], a.v[1], a.v[2], a.v[3]};
+  __builtin_nontemporal_store(q, reinterpret_cast<v4f_t*>(p));
 }
 
 template <int BF16>

@@ -13,8 +13,9 @@
 // 16, .., 1 (lane q < s adds lane q+s: the halving tree; the mirrored lanes
 // compute the same sums since IEEE addition commutes); the block partial is
 // (w0+w1)+(w2+w3) over the four waves, combined through LDS.  The finalize
-// wave gives lane l the partials l, l+64, l+128, ... of the tensor in order,
-// folds, and divides by the element count.  Only magnitudes are added, so
+// folds each group of 256 consecutive block partials of a tensor the same
+// way (partial l in lane l), then one wave gives lane l the group values l,
+// l+64, ... in order, folds, and divides by the element count.  Only magnitudes are added, so
 // the partials are non-negative and independent of sign.
 #include "device.hpp"
 #include "layout.hpp"
@@ -52,10 +53,10 @@ __global__ __launch_bounds__(kThreads) void k_m1_partial(M1Params p) {
         const int64_t idx = static_cast<int64_t>(i0 + u) * p.ld + be.start + loc;
         if (i0 + u < W && nv > 0) {
           if (SRC == 0) {
-            a[u][r] = ld_f32x4(p.x + idx, nv);
+            a[u][r] = ldnt_f32x4(p.x + idx, nv);
           } else {
-            a[u][r] = ld_f32x4(p.m + idx, nv);
-            b[u][r] = ld_x4<GT>(p.g, idx, nv);
+            a[u][r] = ldnt_f32x4(p.m + idx, nv);
+            b[u][r] = ldnt_x4<GT>(p.g, idx, nv);
           }
         } else {
 #pragma unroll
@@ -90,17 +91,34 @@ __global__ __launch_bounds__(kThreads) void k_m1_partial(M1Params p) {
   }
 }
 
-// One wave per (worker, tensor): M1 = fold(lane sums of partials) / n, and
-// scale = Qmax / M1 (0 when M1 == 0, which makes every code 0).
+// Group values: one workgroup per (worker, group of 256 consecutive block
+// partials of one tensor); lane l takes partial l (0.0 past the tensor's last
+// block), each wave folds, then (w0+w1)+(w2+w3).
+__global__ __launch_bounds__(kThreads) void k_m1_group(M1Params p) {
+  __shared__ double sh[4];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int64_t gid = blockIdx.x;
+  const int i = static_cast<int>(gid / p.ngrp), gg = static_cast<int>(gid % p.ngrp);
+  const GroupEnt ge = p.grp[gg];
+  double v = tid < ge.cnt ? p.partial[static_cast<int64_t>(i) * p.nblk + ge.blk + tid] : 0.0;
+  v = wave_fold(v);
+  if (lane == 0) sh[wave] = v;
+  __syncthreads();
+  if (tid == 0) p.gval[static_cast<int64_t>(i) * p.ngrp + gg] = (sh[0] + sh[1]) + (sh[2] + sh[3]);
+}
+
+// One wave per (worker, tensor): lane l sums group values l, l+64, ... in
+// order, the wave folds, M1 = total / n, scale = Qmax / M1 (0 when M1 == 0,
+// which makes every code 0).
 __global__ __launch_bounds__(kThreads) void k_m1_finalize(M1Params p) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t pair = static_cast<int64_t>(blockIdx.x) * 4 + wave;
   if (pair >= static_cast<int64_t>(p.W) * p.nT) return;
   const int i = static_cast<int>(pair / p.nT), T = static_cast<int>(pair % p.nT);
   const TensorEnt te = p.tens[T];
-  const double* P = p.partial + static_cast<int64_t>(i) * p.nblk + te.blk0;
+  const double* G = p.gval + static_cast<int64_t>(i) * p.ngrp + te.grp0;
   double acc = 0.0;
-  for (int k = lane; k < te.nblk; k += kWave) acc = acc + P[k];
+  for (int k = lane; k < te.ngrp; k += kWave) acc = acc + G[k];
   acc = wave_fold(acc);
   if (lane == 0) {
     const double M = acc / static_cast<double>(te.n);
@@ -124,7 +142,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_codes(M1Params p, int8_t* __
       const int nv = max(0, min(kQuad, be.len - loc));
       if (nv == 0) continue;
       const int64_t idx = static_cast<int64_t>(i) * p.ld + be.start + loc;
-      const F4 x = ld_f32x4(p.x + idx, nv);
+      const F4 x = ldnt_f32x4(p.x + idx, nv);
       uint32_t packed = 0;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
@@ -146,6 +164,10 @@ hipError_t launch_m1(const M1Params& p, int src_x, int grad_bf16, hipStream_t st
 }
 
 hipError_t launch_m1_finalize(const M1Params& p, hipStream_t st) {
+  const int64_t groups = static_cast<int64_t>(p.W) * p.ngrp;
+  hipLaunchKernelGGL(k_m1_group, dim3(static_cast<unsigned>(groups)), dim3(kThreads), 0, st, p);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   const int64_t pairs = static_cast<int64_t>(p.W) * p.nT;
   hipLaunchKernelGGL(k_m1_finalize, dim3(static_cast<unsigned>((pairs + 3) / 4)), dim3(kThreads),
                      0, st, p);

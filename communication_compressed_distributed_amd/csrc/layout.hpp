@@ -21,12 +21,23 @@ struct BlockEnt {      // 16 bytes
   int32_t tensor;
 };
 
-struct TensorEnt {     // 32 bytes
+constexpr int kGroup = 256;     // block partials folded together in the finalize
+
+struct TensorEnt {     // 40 bytes
   int64_t off;         // first element
   int64_t n;           // elements
   int32_t blk0;        // first block id
   int32_t nblk;        // blocks
+  int32_t grp0;        // first group id (groups of kGroup consecutive blocks)
+  int32_t ngrp;        // groups
   int32_t sync;        // momentum averaged over workers on averaging steps
+  int32_t pad;
+};
+
+struct GroupEnt {      // 16 bytes: kGroup consecutive blocks of one tensor
+  int32_t tensor;
+  int32_t blk;         // first block id
+  int32_t cnt;         // 1..kGroup
   int32_t pad;
 };
 
@@ -59,7 +70,9 @@ struct M1Params {
   const float* x;      // [W][ld] source c (quant_l1), or
   const float* m;      // [W][ld] with
   const void* g;       // [W][ld]: c = beta1*m + omega1*g
+  const GroupEnt* grp;
   double* partial;     // [W][nblk]
+  double* gval;        // [W][ngrp]
   double* m1;          // [W][nT]
   double* scale;       // [W][nT]
   double* m1_out;      // optional caller copy of m1 [W][nT]
@@ -67,6 +80,7 @@ struct M1Params {
   int32_t W;
   int32_t nT;
   int32_t nblk;
+  int32_t ngrp;
   int32_t qmax;
   float beta1, omega1;
 };

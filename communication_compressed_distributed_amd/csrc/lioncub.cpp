@@ -34,20 +34,24 @@ namespace {
 constexpr size_t kWsAlign = 256;
 
 struct WsLayout {
-  size_t blk, tens, partial, m1, scale, total;
+  size_t blk, tens, grp, partial, gval, m1, scale, total;
 };
 
 size_t align_up(size_t x) { return (x + kWsAlign - 1) / kWsAlign * kWsAlign; }
 
-WsLayout ws_layout(int64_t nblk, int64_t nT, int64_t W) {
+WsLayout ws_layout(int64_t nblk, int64_t ngrp, int64_t nT, int64_t W) {
   WsLayout L;
   size_t o = 0;
   L.blk = o;
   o = align_up(o + static_cast<size_t>(nblk) * sizeof(BlockEnt));
   L.tens = o;
   o = align_up(o + static_cast<size_t>(nT) * sizeof(TensorEnt));
+  L.grp = o;
+  o = align_up(o + static_cast<size_t>(ngrp) * sizeof(GroupEnt));
   L.partial = o;
   o = align_up(o + static_cast<size_t>(W * nblk) * sizeof(double));
+  L.gval = o;
+  o = align_up(o + static_cast<size_t>(W * ngrp) * sizeof(double));
   L.m1 = o;
   o = align_up(o + static_cast<size_t>(W * nT) * sizeof(double));
   L.scale = o;
@@ -58,8 +62,9 @@ WsLayout ws_layout(int64_t nblk, int64_t nT, int64_t W) {
 
 bool finite(float x) { return std::isfinite(x); }
 
-// Checks every field; on success *nblk = number of tensor-aligned blocks.
-int check_config(const lioncub_config* c, int64_t* nblk) {
+// Checks every field; on success *nblk = number of tensor-aligned blocks and
+// *ngrp = number of groups of kGroup consecutive blocks (per tensor).
+int check_config(const lioncub_config* c, int64_t* nblk, int64_t* ngrp) {
   if (!c) return LIONCUB_EINVAL;
   if (c->d < 1 || c->ld < c->d || c->ld % 64 != 0) return LIONCUB_EINVAL;
   if (c->W < 1 || c->W > 255) return LIONCUB_EINVAL;
@@ -75,13 +80,16 @@ int check_config(const lioncub_config* c, int64_t* nblk) {
     return LIONCUB_EINVAL;
   const int64_t* off = c->tensor_offsets;
   if (off[0] != 0 || off[c->n_tensors] != c->d) return LIONCUB_EINVAL;
-  int64_t nb = 0;
+  int64_t nb = 0, ng = 0;
   for (int k = 0; k < c->n_tensors; ++k) {
     if (off[k + 1] <= off[k] || off[k] % 64 != 0) return LIONCUB_EINVAL;
-    nb += (off[k + 1] - off[k] + kBlock - 1) / kBlock;
+    const int64_t b = (off[k + 1] - off[k] + kBlock - 1) / kBlock;
+    nb += b;
+    ng += (b + kGroup - 1) / kGroup;
   }
   if (nb > 0x7FFFFFFF) return LIONCUB_EUNSUPPORTED;
   *nblk = nb;
+  *ngrp = ng;
   return LIONCUB_OK;
 }
 
@@ -93,13 +101,17 @@ struct lioncub_ctx {
   lioncub_config cfg;  // host pointers cleared after init
   hipStream_t stream;
   int32_t nblk;
+  int32_t ngrp;
   BlockEnt* blk;
   TensorEnt* tens;
+  GroupEnt* grp;
   double* partial;
+  double* gval;
   double* m1;
   double* scale;
   std::vector<BlockEnt> h_blk;
   std::vector<TensorEnt> h_tens;
+  std::vector<GroupEnt> h_grp;
   // profiling hook
   bool prof = false;
   int32_t prof_cap = 0;
@@ -147,13 +159,16 @@ void fill_m1_params(const lioncub_ctx* c, M1Params* p) {
   std::memset(p, 0, sizeof(*p));
   p->blk = c->blk;
   p->tens = c->tens;
+  p->grp = c->grp;
   p->partial = c->partial;
+  p->gval = c->gval;
   p->m1 = c->m1;
   p->scale = c->scale;
   p->ld = c->cfg.ld;
   p->W = c->cfg.W;
   p->nT = c->cfg.n_tensors;
   p->nblk = c->nblk;
+  p->ngrp = c->ngrp;
   p->qmax = c->cfg.qbits >= 2 && c->cfg.qbits <= 8 ? (1 << (c->cfg.qbits - 1)) - 1 : 0;
   p->beta1 = c->cfg.beta1;
   p->omega1 = 1.0f - c->cfg.beta1;
@@ -166,19 +181,19 @@ int dev_status(hipError_t e) { return e == hipSuccess ? LIONCUB_OK : LIONCUB_EDE
 extern "C" {
 
 size_t lioncub_workspace_bytes(const lioncub_config* cfg) {
-  int64_t nblk = 0;
-  if (check_config(cfg, &nblk) != LIONCUB_OK) return 0;
-  return ws_layout(nblk, cfg->n_tensors, cfg->W).total;
+  int64_t nblk = 0, ngrp = 0;
+  if (check_config(cfg, &nblk, &ngrp) != LIONCUB_OK) return 0;
+  return ws_layout(nblk, ngrp, cfg->n_tensors, cfg->W).total;
 }
 
 int lioncub_init(lioncub_ctx** out, const lioncub_config* cfg, void* hip_stream, void* workspace,
                  size_t ws_bytes) {
   if (!out) return LIONCUB_EINVAL;
   *out = nullptr;
-  int64_t nblk = 0;
-  int st = check_config(cfg, &nblk);
+  int64_t nblk = 0, ngrp = 0;
+  int st = check_config(cfg, &nblk, &ngrp);
   if (st != LIONCUB_OK) return st;
-  const WsLayout L = ws_layout(nblk, cfg->n_tensors, cfg->W);
+  const WsLayout L = ws_layout(nblk, ngrp, cfg->n_tensors, cfg->W);
   if (!workspace || !aligned(workspace, kWsAlign) || ws_bytes < L.total) return LIONCUB_EWORKSPACE;
 
   lioncub_ctx* c = new (std::nothrow) lioncub_ctx();
@@ -186,15 +201,19 @@ int lioncub_init(lioncub_ctx** out, const lioncub_config* cfg, void* hip_stream,
   c->cfg = *cfg;
   c->stream = static_cast<hipStream_t>(hip_stream);
   c->nblk = static_cast<int32_t>(nblk);
+  c->ngrp = static_cast<int32_t>(ngrp);
   char* ws = static_cast<char*>(workspace);
   c->blk = reinterpret_cast<BlockEnt*>(ws + L.blk);
   c->tens = reinterpret_cast<TensorEnt*>(ws + L.tens);
+  c->grp = reinterpret_cast<GroupEnt*>(ws + L.grp);
   c->partial = reinterpret_cast<double*>(ws + L.partial);
+  c->gval = reinterpret_cast<double*>(ws + L.gval);
   c->m1 = reinterpret_cast<double*>(ws + L.m1);
   c->scale = reinterpret_cast<double*>(ws + L.scale);
 
   c->h_tens.resize(cfg->n_tensors);
   c->h_blk.reserve(nblk);
+  c->h_grp.reserve(ngrp);
   for (int T = 0; T < cfg->n_tensors; ++T) {
     const int64_t a = cfg->tensor_offsets[T], n = cfg->tensor_offsets[T + 1] - a;
     TensorEnt& te = c->h_tens[T];
@@ -202,8 +221,18 @@ int lioncub_init(lioncub_ctx** out, const lioncub_config* cfg, void* hip_stream,
     te.n = n;
     te.blk0 = static_cast<int32_t>(c->h_blk.size());
     te.nblk = static_cast<int32_t>((n + kBlock - 1) / kBlock);
+    te.grp0 = static_cast<int32_t>(c->h_grp.size());
+    te.ngrp = (te.nblk + kGroup - 1) / kGroup;
     te.sync = cfg->sync_m ? (cfg->sync_m[T] ? 1 : 0) : 0;
     te.pad = 0;
+    for (int32_t gq = 0; gq < te.ngrp; ++gq) {
+      GroupEnt ge;
+      ge.tensor = T;
+      ge.blk = te.blk0 + gq * kGroup;
+      ge.cnt = te.nblk - gq * kGroup < kGroup ? te.nblk - gq * kGroup : kGroup;
+      ge.pad = 0;
+      c->h_grp.push_back(ge);
+    }
     for (int64_t s = 0; s < n; s += kBlock) {
       BlockEnt be;
       be.start = a + s;
@@ -219,6 +248,9 @@ int lioncub_init(lioncub_ctx** out, const lioncub_config* cfg, void* hip_stream,
                                 hipMemcpyHostToDevice, c->stream);
   if (e == hipSuccess)
     e = hipMemcpyAsync(c->tens, c->h_tens.data(), c->h_tens.size() * sizeof(TensorEnt),
+                       hipMemcpyHostToDevice, c->stream);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(c->grp, c->h_grp.data(), c->h_grp.size() * sizeof(GroupEnt),
                        hipMemcpyHostToDevice, c->stream);
   if (e == hipSuccess) e = hipStreamSynchronize(c->stream);
   if (e != hipSuccess) {

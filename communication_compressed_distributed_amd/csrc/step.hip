@@ -29,147 +29,167 @@
 
 namespace lioncub {
 
-// One round of one thread: its quad at element j (nv of 4 valid), all
-// workers.  FULL rounds (every lane of the workgroup has a whole quad) take
-// straight vector loads with no per-lane predicates; WT > 0 fixes W at compile
-// time so the worker loop has no bounds tests.
-template <int TT, int GT, bool DBG, int AGG, int WB, int WT, bool FULL>
-__device__ __forceinline__ void step_round(const StepParams& p, int tensor, int64_t j, int nv,
-                                           bool avg, uint32_t par) {
+// One workgroup, one block.  Each thread owns the quads j[q] = start +
+// 1024*q + 4*tid (q = 0..3) and walks the workers in the outer loop, so each
+// worker row is read as one 16 KB contiguous run per workgroup before the
+// next row (measured: longer runs per row stream better than interleaving
+// the rows quad by quad).  FULL blocks (all 4096 elements present) have no
+// per-lane predicates; WT > 0 fixes W at compile time; AVG selects the
+// averaging path (new momenta summed, their mean written to every worker).
+template <int TT, int GT, bool DBG, int AGG, int WB, int WT, bool FULL, bool AVG>
+__device__ __forceinline__ void step_block(const StepParams& p, const BlockEnt& be, uint32_t par) {
+  constexpr int Q = kRounds;
   const int W = WT > 0 ? WT : p.W;
-  if (FULL) nv = kQuad;
   const int tid = threadIdx.x;
-  const double* __restrict__ scl = p.scale + tensor;  // scl[i*nT]
+  const double* __restrict__ scl = p.scale + be.tensor;  // scl[i*nT]
   float* __restrict__ m = p.m;
 
-  // theta does not change until the end of the round: fetch it first
-  F4 th;
-  if (FULL || nv > 0) th = ld_x4<TT>(p.theta, j, nv);
+  int64_t j[Q];
+  int nv[Q];
+#pragma unroll
+  for (int q = 0; q < Q; ++q) {
+    const int loc = kThreads * kQuad * q + kQuad * tid;
+    j[q] = be.start + loc;
+    nv[q] = FULL ? kQuad : max(0, min(kQuad, be.len - loc));
+  }
 
-  uint32_t cnt = 0;           // vote: per-element counts, one byte each
-  int sum[4] = {0, 0, 0, 0};  // L1: per-element integer sums
-  F4 acc;                     // averaging: running sum of new momenta
+  // theta does not change until the end: fetch it first
+  F4 th[Q];
+#pragma unroll
+  for (int q = 0; q < Q; ++q)
+    if (FULL || nv[q] > 0) th[q] = ld_x4<TT>(p.theta, j[q], nv[q]);
 
+  uint32_t cnt[Q];    // vote: per-element counts, one byte each
+  int sum[Q][4];      // L1: per-element integer sums
+  F4 acc[Q];          // averaging: running sum of new momenta
+#pragma unroll
+  for (int q = 0; q < Q; ++q) {
+    cnt[q] = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) sum[q][k] = 0;
+  }
+
+  constexpr bool kExact = WT > 0 && WT % WB == 0;
 #pragma unroll 1
   for (int i0 = 0; i0 < W; i0 += WB) {
-    F4 mv[WB], gv[WB];
+    F4 mv[WB][Q], gv[WB][Q];
 #pragma unroll
     for (int b = 0; b < WB; ++b) {
-      if ((WT > 0 && WT % WB == 0) || i0 + b < W) {
-        if (FULL || nv > 0) {
-          const int64_t idx = static_cast<int64_t>(i0 + b) * p.ld + j;
-          mv[b] = ld_f32x4(m + idx, nv);
-          gv[b] = ld_x4<GT>(p.g, idx, nv);
-          continue;
+#pragma unroll
+      for (int q = 0; q < Q; ++q) {
+        if ((kExact || i0 + b < W) && (FULL || nv[q] > 0)) {
+          const int64_t idx = static_cast<int64_t>(i0 + b) * p.ld + j[q];
+          mv[b][q] = ldnt_f32x4(m + idx, nv[q]);
+          gv[b][q] = ldnt_x4<GT>(p.g, idx, nv[q]);
+        } else {
+#pragma unroll
+          for (int k = 0; k < 4; ++k) mv[b][q].v[k] = gv[b][q].v[k] = 0.0f;
         }
       }
-#pragma unroll
-      for (int k = 0; k < 4; ++k) mv[b].v[k] = gv[b].v[k] = 0.0f;
     }
 #pragma unroll
     for (int b = 0; b < WB; ++b) {
       const int i = i0 + b;
-      if (!(WT > 0 && WT % WB == 0) && i >= W) break;
-      const int64_t idx = static_cast<int64_t>(i) * p.ld + j;
-      F4 mn;
-      uint32_t nib = 0;
+      if (!kExact && i >= W) break;
       double s_i = 0.0;
       if (AGG == 1) s_i = scl[static_cast<int64_t>(i) * p.nT];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const float c = (p.beta1 * mv[b].v[k]) + (p.omega1 * gv[b].v[k]);
-        if (AGG == 0) {
-          nib |= ((FULL || k < nv) ? sign_bit(c, par) : 0u) << k;
-        } else {
-          double y = __builtin_rint(static_cast<double>(c) * s_i);
-          y = fmin(fmax(y, -static_cast<double>(p.qmax)), static_cast<double>(p.qmax));
-          const int q = static_cast<int>(y);
-          sum[k] += q;
-          if (DBG) nib |= (static_cast<uint32_t>(q) & 0xFFu) << (8 * k);
-        }
-        mn.v[k] = (p.beta2 * mv[b].v[k]) + (p.omega2 * gv[b].v[k]);
-      }
-      if (AGG == 0) {
-        cnt += nibble_to_bytes(nib);
-        if (DBG && p.bits) {
-          const uint64_t word = wave_pack_words(nib);
-          if ((tid & 15) == 0 && (FULL || nv > 0))
-            p.bits[static_cast<int64_t>(i) * (p.ld >> 6) + (j >> 6)] = word;
-        }
-      } else if (DBG && p.codes && (FULL || nv > 0)) {
-        st_b4(p.codes + idx, nib, nv);
-      }
-      if (FULL || nv > 0) {
-        if (!avg) {
-          st_f32x4(m + idx, mn, nv);
-        } else if (i == 0) {
-          acc = mn;
-        } else {
+      for (int q = 0; q < Q; ++q) {
+        const int64_t idx = static_cast<int64_t>(i) * p.ld + j[q];
+        F4 mn;
+        uint32_t nib = 0;
 #pragma unroll
-          for (int k = 0; k < 4; ++k) acc.v[k] = acc.v[k] + mn.v[k];
+        for (int k = 0; k < 4; ++k) {
+          const float c = (p.beta1 * mv[b][q].v[k]) + (p.omega1 * gv[b][q].v[k]);
+          if (AGG == 0) {
+            nib |= ((FULL || k < nv[q]) ? sign_bit(c, par) : 0u) << k;
+          } else {
+            double y = __builtin_rint(static_cast<double>(c) * s_i);
+            y = fmin(fmax(y, -static_cast<double>(p.qmax)), static_cast<double>(p.qmax));
+            const int qc = static_cast<int>(y);
+            sum[q][k] += qc;
+            if (DBG) nib |= (static_cast<uint32_t>(qc) & 0xFFu) << (8 * k);
+          }
+          mn.v[k] = (p.beta2 * mv[b][q].v[k]) + (p.omega2 * gv[b][q].v[k]);
+        }
+        if (AGG == 0) {
+          cnt[q] += nibble_to_bytes(nib);
+          if (DBG && p.bits) {
+            const uint64_t word = wave_pack_words(nib);  // every lane takes part
+            if ((tid & 15) == 0 && (FULL || nv[q] > 0))
+              p.bits[static_cast<int64_t>(i) * (p.ld >> 6) + (j[q] >> 6)] = word;
+          }
+        } else if (DBG && p.codes && (FULL || nv[q] > 0)) {
+          st_b4(p.codes + idx, nib, nv[q]);
+        }
+        if (FULL || nv[q] > 0) {
+          if (!AVG) {
+            stnt_f32x4(m + idx, mn, nv[q]);
+          } else if (i == 0) {
+            acc[q] = mn;
+          } else {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) acc[q].v[k] = acc[q].v[k] + mn.v[k];
+          }
         }
       }
     }
   }
-  if (!FULL && nv == 0) return;
 
-  // global sign
-  int s[4];
-  if (AGG == 0) {
+#pragma unroll
+  for (int q = 0; q < Q; ++q) {
+    if (!FULL && nv[q] == 0) continue;
+    // global sign
+    int s[4];
+    if (AGG == 0) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int twice = 2 * static_cast<int>((cnt[q] >> (8 * k)) & 0xFFu);
+        s[k] = twice > W ? 1 : (twice < W ? -1 : (p.tie_zero ? 0 : (par ? 1 : -1)));
+      }
+      if (DBG && p.counts) st_b4(p.counts + j[q], cnt[q], nv[q]);
+    } else {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) s[k] = (sum[q][k] > 0) - (sum[q][k] < 0);
+      if (DBG && p.sums) st_i32x4(p.sums + j[q], sum[q], nv[q]);
+    }
+    if (DBG && p.sign) {
+      const uint32_t packed = (static_cast<uint32_t>(s[0]) & 0xFFu) |
+                              ((static_cast<uint32_t>(s[1]) & 0xFFu) << 8) |
+                              ((static_cast<uint32_t>(s[2]) & 0xFFu) << 16) |
+                              ((static_cast<uint32_t>(s[3]) & 0xFFu) << 24);
+      st_b4(p.sign + j[q], packed, nv[q]);
+    }
+    // theta <- theta - lr*(sign + wd*theta)
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const int twice = 2 * static_cast<int>((cnt >> (8 * k)) & 0xFFu);
-      s[k] = twice > W ? 1 : (twice < W ? -1 : (p.tie_zero ? 0 : (par ? 1 : -1)));
+      const float x = th[q].v[k];
+      th[q].v[k] = x - (p.lr * (static_cast<float>(s[k]) + (p.wd * x)));
     }
-    if (DBG && p.counts) st_b4(p.counts + j, cnt, nv);
-  } else {
+    st_x4<TT>(p.theta, j[q], th[q], nv[q]);
+    // worker mean of the new momenta on averaging steps
+    if (AVG) {
+      const float fw = static_cast<float>(W);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) s[k] = (sum[k] > 0) - (sum[k] < 0);
-    if (DBG && p.sums) st_i32x4(p.sums + j, sum, nv);
-  }
-  if (DBG && p.sign) {
-    const uint32_t packed = (static_cast<uint32_t>(s[0]) & 0xFFu) |
-                            ((static_cast<uint32_t>(s[1]) & 0xFFu) << 8) |
-                            ((static_cast<uint32_t>(s[2]) & 0xFFu) << 16) |
-                            ((static_cast<uint32_t>(s[3]) & 0xFFu) << 24);
-    st_b4(p.sign + j, packed, nv);
-  }
-
-  // theta <- theta - lr*(sign + wd*theta)
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const float x = th.v[k];
-    th.v[k] = x - (p.lr * (static_cast<float>(s[k]) + (p.wd * x)));
-  }
-  st_x4<TT>(p.theta, j, th, nv);
-
-  // worker mean of the new momenta on averaging steps
-  if (avg) {
-    const float fw = static_cast<float>(W);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) acc.v[k] = acc.v[k] / fw;
+      for (int k = 0; k < 4; ++k) acc[q].v[k] = acc[q].v[k] / fw;
 #pragma unroll 4
-    for (int i = 0; i < W; ++i) st_f32x4(m + static_cast<int64_t>(i) * p.ld + j, acc, nv);
+      for (int i = 0; i < W; ++i)
+        stnt_f32x4(m + static_cast<int64_t>(i) * p.ld + j[q], acc[q], nv[q]);
+    }
   }
 }
 
 template <int TT, int GT, bool DBG, int AGG, int WB, int WT>
 __global__ __launch_bounds__(kThreads) void k_step(StepParams p) {
   const BlockEnt be = p.blk[blockIdx.x];
-  const int tid = threadIdx.x;
   const bool avg = p.avg_step && p.tens[be.tensor].sync;
   const uint32_t par = static_cast<uint32_t>(p.parity);
-#pragma unroll 1
-  for (int r = 0; r < kRounds; ++r) {
-    const int base = kThreads * kQuad * r;
-    const int rem = be.len - base;  // uniform over the workgroup
-    const int64_t j = be.start + base + kQuad * tid;
-    if (rem >= kThreads * kQuad) {
-      step_round<TT, GT, DBG, AGG, WB, WT, true>(p, be.tensor, j, kQuad, avg, par);
-    } else if (rem > 0) {
-      const int nv = max(0, min(kQuad, rem - kQuad * tid));
-      if (DBG || nv > 0) step_round<TT, GT, DBG, AGG, WB, 0, false>(p, be.tensor, j, nv, avg, par);
-    }
+  if (be.len == kBlock) {
+    if (avg) step_block<TT, GT, DBG, AGG, WB, WT, true, true>(p, be, par);
+    else step_block<TT, GT, DBG, AGG, WB, WT, true, false>(p, be, par);
+  } else {
+    if (avg) step_block<TT, GT, DBG, AGG, WB, 0, false, true>(p, be, par);
+    else step_block<TT, GT, DBG, AGG, WB, 0, false, false>(p, be, par);
   }
 }
 
@@ -182,14 +202,14 @@ __global__ void k_zero_tail_words(uint64_t* bits, int64_t words, int64_t first, 
   bits[i * words + w] = 0;
 }
 
-constexpr int kWB = 8;
+constexpr int kWB = 2;
 
 template <int TT, int GT, bool DBG, int AGG>
 static hipError_t launch_t(const StepParams& p, int nblk, hipStream_t st) {
   const dim3 g(nblk), b(kThreads);
   if constexpr (!DBG) {
     if (p.W == 4) {
-      hipLaunchKernelGGL((k_step<TT, GT, DBG, AGG, 4, 4>), g, b, 0, st, p);
+      hipLaunchKernelGGL((k_step<TT, GT, DBG, AGG, kWB, 4>), g, b, 0, st, p);
       return hipGetLastError();
     }
     if (p.W == 8) {

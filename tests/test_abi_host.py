@@ -40,15 +40,18 @@ def cfg(**kw):
 
 
 def test_workspace_bytes_layout():
-    # blocks: ceil(4096/4096) + ceil(5904/4096) = 3; 256-byte aligned pieces
+    # blocks: ceil(4096/4096) + ceil(5904/4096) = 3, one group of block
+    # partials per tensor; 256-byte aligned pieces
     c = cfg()
     n = _abi.lioncub_workspace_bytes(c)
     blk = 3 * 16
-    tens = 2 * 32
+    tens = 2 * 40
+    grp = 2 * 16
     part = 4 * 3 * 8
+    gval = 4 * 2 * 8
     m1 = 4 * 2 * 8
     al = lambda x: (x + 255) // 256 * 256
-    assert n == al(blk) + al(tens) + al(part) + 2 * al(m1)
+    assert n == al(blk) + al(tens) + al(grp) + al(part) + al(gval) + 2 * al(m1)
     big = cfg(d=1_313_626_112, ld=1_313_626_112, W=8,
               tensor_offsets=[0, 1_000_000_000 // 64 * 64, 1_313_626_112])
     assert _abi.lioncub_workspace_bytes(big) > 0
