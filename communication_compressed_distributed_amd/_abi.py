@@ -36,7 +36,7 @@ class lioncub_config(C.Structure):
 
 class lioncub_debug(C.Structure):
     _fields_ = [("bits", C.c_void_p), ("codes", C.c_void_p), ("counts", C.c_void_p),
-                ("sums", C.c_void_p), ("sign", C.c_void_p)]
+                ("sums", C.c_void_p), ("sign", C.c_void_p), ("m1", C.c_void_p)]
 
 
 _lib = None
@@ -140,7 +140,7 @@ def lioncub_step(ctx, theta, m, g, t, dbg=None):
     d = None
     if dbg is not None:
         d = lioncub_debug(*(None if dbg.get(k) is None else dbg[k].data_ptr()
-                            for k in ("bits", "codes", "counts", "sums", "sign")))
+                            for k in ("bits", "codes", "counts", "sums", "sign", "m1")))
     _check("lioncub_step", lib().lioncub_step(ctx, _ptr(theta), _ptr(m), _ptr(g), int(t),
                                               C.byref(d) if d is not None else None))
 

@@ -282,9 +282,9 @@ int lioncub_step(lioncub_ctx* ctx, void* theta, float* m, const void* g, int64_t
   p.avg_step = (t % cf.sync_every) == 0;
   if (dbg) {
     if ((dbg->bits || dbg->counts) && l1) return LIONCUB_EINVAL;
-    if ((dbg->codes || dbg->sums) && !l1) return LIONCUB_EINVAL;
+    if ((dbg->codes || dbg->sums || dbg->m1) && !l1) return LIONCUB_EINVAL;
     if (!aligned(dbg->bits, 16) || !aligned(dbg->codes, 16) || !aligned(dbg->counts, 16) ||
-        !aligned(dbg->sums, 16) || !aligned(dbg->sign, 16))
+        !aligned(dbg->sums, 16) || !aligned(dbg->sign, 16) || !aligned(dbg->m1, 16))
       return LIONCUB_EALIGN;
     p.bits = dbg->bits;
     p.codes = dbg->codes;
@@ -298,6 +298,7 @@ int lioncub_step(lioncub_ctx* ctx, void* theta, float* m, const void* g, int64_t
     fill_m1_params(ctx, &q);
     q.m = m;
     q.g = g;
+    q.m1_out = dbg ? dbg->m1 : nullptr;
     e = run(ctx, LIONCUB_K_M1_PARTIAL, [&] { return launch_m1(q, 0, cf.grad_dtype, ctx->stream); });
     if (e == hipSuccess)
       e = run(ctx, LIONCUB_K_M1_FINALIZE, [&] { return launch_m1_finalize(q, ctx->stream); });

@@ -98,6 +98,8 @@ typedef struct {
   uint8_t *counts; /* device [d]: number of +1 bits per element (vote path)     */
   int32_t *sums;   /* device [d]: integer sum of the codes (L1 path)            */
   int8_t *sign;    /* device [d]: the global sign applied, in {-1, 0, +1}       */
+  double *m1;      /* device [W][n_tensors]: mean |c| per (worker, tensor)
+                      (L1 path); does not change which step kernel runs     */
 } lioncub_debug;
 
 /* Bytes of device workspace lioncub_init needs for cfg (0 if cfg is invalid).
@@ -121,7 +123,8 @@ int lioncub_set_stream(lioncub_ctx *ctx, void *hip_stream);
  *   g:     device [W][ld], fp32 or bf16 per grad_dtype (read only)
  *   t:     1-based step index; decides zero and tie parity and averaging steps
  *   dbg:   NULL, or optional outputs (bits/counts on the vote path,
- *          codes/sums on the L1 path, sign on both)
+ *          codes/sums/m1 on the L1 path, sign on both); an output of the other
+ *          path is an error (LIONCUB_EINVAL)
  * The vote path is one kernel; the L1 path is three (mean |c| block partials,
  * per-(worker, tensor) mean and scale, then the fused quantise-sum-apply). */
 int lioncub_step(lioncub_ctx *ctx, void *theta, float *m, const void *g, int64_t t,

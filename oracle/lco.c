@@ -214,6 +214,19 @@ void lco_c_row(const lco_cfg *cfg, int64_t n, const float *m, const void *g,
     c[k] = (cfg->beta1 * m[k]) + (omega1 * load_g(cfg, g, k));
 }
 
+void lco_m1_partials(const lco_cfg *cfg, int64_t n, const float *m, const void *g,
+                     double *P) {
+  float c[LCO_M1_BLOCK];
+  size_t gsz = cfg->grad_bf16 ? 2 : 4;
+  for (int64_t b = 0; b * LCO_M1_BLOCK < n; b++) {
+    int64_t len = n - b * LCO_M1_BLOCK;
+    if (len > LCO_M1_BLOCK) len = LCO_M1_BLOCK;
+    lco_c_row(cfg, len, m + b * LCO_M1_BLOCK,
+              (const char *)g + (size_t)(b * LCO_M1_BLOCK) * gsz, c);
+    P[b] = lco_m1_block(c, len);
+  }
+}
+
 void lco_m1_all(const lco_cfg *cfg, int64_t ld, const float *m, const void *g,
                 double *m1) {
   size_t gsz = cfg->grad_bf16 ? 2 : 4;

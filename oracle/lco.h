@@ -105,6 +105,12 @@ void lco_quant_l1(const lco_cfg *cfg, int64_t ld, const float *x,
 void lco_c_row(const lco_cfg *cfg, int64_t n, const float *m, const void *g,
                float *c);
 
+/* Block partials of n consecutive elements of one worker's row, starting at
+ * a block boundary of its tensor: P[b] for the ceil(n/4096) blocks, c formed
+ * from m and g as in lco_c_row.  Lets a caller stream a row in chunks. */
+void lco_m1_partials(const lco_cfg *cfg, int64_t n, const float *m, const void *g,
+                     double *P);
+
 /* M1 of every (worker, tensor) from the full state: m1[W][n_tensors]. */
 void lco_m1_all(const lco_cfg *cfg, int64_t ld, const float *m, const void *g,
                 double *m1);

@@ -61,6 +61,7 @@ def lib():
         L.lco_quant_l1.argtypes = [C.POINTER(Cfg), i64, vp, vp, vp]
         L.lco_c_row.argtypes = [C.POINTER(Cfg), i64, vp, vp, vp]
         L.lco_m1_all.argtypes = [C.POINTER(Cfg), i64, vp, vp, vp]
+        L.lco_m1_partials.argtypes = [C.POINTER(Cfg), i64, vp, vp, vp]
         L.lco_step_range.argtypes = [C.POINTER(Cfg), i64, i64, vp, vp, vp, vp, i64, i64,
                                      C.POINTER(Debug)]
         L.lco_step.argtypes = [C.POINTER(Cfg), i64, vp, vp, vp, i64, C.POINTER(Debug)]
@@ -176,6 +177,16 @@ def m1_all(wl, m, g):
     g = np.ascontiguousarray(g)
     out = np.empty((wl.W, wl.n_tensors), dtype=np.float64)
     lib().lco_m1_all(cfg.ref, m.shape[1], _p(m), _p(g), _p(out))
+    return out
+
+
+def m1_partials(wl, m_row, g_row):
+    """Block partials of a block-aligned run of one worker's row."""
+    cfg = OracleCfg(wl)
+    m_row = np.ascontiguousarray(m_row, dtype=np.float32)
+    g_row = np.ascontiguousarray(g_row)
+    out = np.empty((m_row.size + M1_BLOCK - 1) // M1_BLOCK, dtype=np.float64)
+    lib().lco_m1_partials(cfg.ref, m_row.size, _p(m_row), _p(g_row), _p(out))
     return out
 
 

@@ -1,0 +1,126 @@
+"""Full-size parity: the five workloads at their real sizes, run with the
+production kernels bench.py times, checked against the CPU oracle on sampled
+column ranges (first, last -- the ragged end --, tensor boundaries and random
+interior ranges).  On the L1 workloads the oracle first recomputes M1 from
+the pre-step state, streamed from the device one worker row at a time, for
+every (worker, tensor) pair the samples touch (all of them for the flat 350M
+model), and M1 itself is compared bit for bit with the library's."""
+import numpy as np
+import pytest
+
+from oracle import lco
+from synth import gen
+from synth import workloads as wls
+from tests.harness import check_float_state, lioncub_for, to_host
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+
+STREAM = 1 << 24  # elements per host round trip when recomputing M1
+
+
+def _say(*a):
+    print("[fullsize]", *a, flush=True)
+
+
+def sample_ranges(wl, tensors, rs, width=65536, n_random=6):
+    """Column ranges inside the given tensors: each tensor's start, its end
+    and one random interior range (all within the tensor)."""
+    out = []
+    off = wl.offsets
+    for T in tensors:
+        a, b = off[T], off[T + 1]
+        w = min(width, b - a)
+        out.append((a, a + w))
+        out.append((b - w, b))
+        for _ in range(n_random):
+            if b - a > 2 * w:
+                s = int(rs.integers(a, b - w)) // 64 * 64
+                out.append((s, s + w))
+    return sorted(set(out))
+
+
+def oracle_m1(wl, m, g, pairs):
+    """M1[i][T] for the requested (worker, tensor) pairs from device state."""
+    off = wl.offsets
+    res = {}
+    for (i, T) in pairs:
+        a, b = off[T], off[T + 1]
+        parts = []
+        for s in range(a, b, STREAM):
+            e = min(b, s + STREAM)
+            parts.append(lco.m1_partials(wl, to_host(m[i, s:e]), to_host(g[i, s:e])))
+        res[(i, T)] = lco.m1_finalize(np.concatenate(parts), b - a)
+    return res
+
+
+def run_fullsize(wl, steps, tensors=None, n_random=6):
+    import torch
+    torch.cuda.set_device(0)
+    rs = np.random.default_rng(7)
+    tensors = list(range(wl.n_tensors)) if tensors is None else tensors
+    ranges = sample_ranges(wl, tensors, rs, n_random=n_random)
+    _say(wl.name, f"d={wl.d} W={wl.W} ranges={len(ranges)} tensors={len(tensors)}")
+    theta = gen.device_theta(wl)
+    m = gen.device_m(wl)
+    g = gen.device_g(wl, steps[0])
+    lc = lioncub_for(wl)
+    tb = wl.theta_dtype == "bf16"
+    for t in steps:
+        gen.fill_device_g(wl, t, g)
+        torch.cuda.synchronize()
+        pre = [(j0, j1, to_host(theta[j0:j1]).copy(), to_host(m[:, j0:j1]).copy(),
+                to_host(g[:, j0:j1]).copy()) for j0, j1 in ranges]
+        m1v = None
+        dbg = None
+        if wl.agg == "l1":
+            pairs = [(i, T) for i in range(wl.W) for T in tensors]
+            want_m1 = oracle_m1(wl, m, g, pairs)
+            _say(wl.name, f"t={t} oracle M1 done for {len(pairs)} pairs")
+            m1v = np.full((wl.W, wl.n_tensors), np.nan)
+            for (i, T), v in want_m1.items():
+                m1v[i, T] = v
+            dbg = {"m1": torch.zeros((wl.W, wl.n_tensors), dtype=torch.float64, device="cuda")}
+        lc.step(theta, m, g, t, dbg)
+        torch.cuda.synchronize()
+        if dbg is not None:
+            got = to_host(dbg["m1"])
+            for (i, T), v in want_m1.items():
+                assert np.float64(got[i, T]).view(np.uint64) == np.float64(v).view(np.uint64), \
+                    (i, T, got[i, T], v)
+        for j0, j1, th, mc, gc in pre:
+            mc = np.ascontiguousarray(mc)
+            lco.step_range(wl, j0, j1, m1v, th, mc, np.ascontiguousarray(gc), t)
+            check_float_state(f"theta[{j0}:{j1}] t={t}", to_host(theta[j0:j1]), th, bf16=tb)
+            check_float_state(f"m[:, {j0}:{j1}] t={t}", to_host(m[:, j0:j1]), mc)
+        _say(wl.name, f"t={t} ok")
+    lc.close()
+    del theta, m, g
+    torch.cuda.empty_cache()
+
+
+def test_flat_1M_w4_vote_fullsize():
+    run_fullsize(wls.FLAT_1M_W4_VOTE, steps=list(range(1, 11)))
+
+
+def test_gpt2_124M_w8_vote_fullsize():
+    wl = wls.GPT2_124M_W8_VOTE
+    run_fullsize(wl, steps=[1, 2], n_random=1)
+
+
+def test_flat_350M_w16_l1q4_fullsize():
+    run_fullsize(wls.FLAT_350M_W16_L1Q4, steps=[1, 2])
+
+
+def test_gpt_760M_w8_vote_bf16_sync_fullsize():
+    wl = wls.GPT_760M_W8_VOTE_SYNC
+    run_fullsize(wl, steps=[1, 2, 3], n_random=1)
+
+
+def test_gpt_1B3_w8_l1q8_bf16g_fullsize():
+    """M1 recomputed on the host for the embeddings, the first and last
+    transformer blocks and the final LayerNorm (the samples' tensors)."""
+    wl = wls.GPT_1B3_W8_L1Q8
+    names = [nm for nm, _ in wl.tensors]
+    pick = [k for k, nm in enumerate(names)
+            if nm in ("wte", "wpe", "ln_f.w", "ln_f.b") or nm.startswith(("h0.", "h23."))]
+    run_fullsize(wl, steps=[1, 2], tensors=pick, n_random=1)
