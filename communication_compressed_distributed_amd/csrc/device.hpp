@@ -61,6 +61,30 @@ __device__ __forceinline__ F4 ld_x4(const void* __restrict__ base, int64_t idx, 
   return ld_f32x4(static_cast<const float*>(base) + idx, nv);
 }
 
+// Element-wise masked quad loads for ragged blocks: no vector/scalar branch,
+// so lanes of one wave that hold whole and partial quads share one path.
+__device__ __forceinline__ F4 ldm_f32x4(const float* __restrict__ p, int nv) {
+  F4 r;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) r.v[k] = k < nv ? p[k] : 0.0f;
+  return r;
+}
+
+template <int BF16>
+__device__ __forceinline__ F4 ldm_x4(const void* __restrict__ base, int64_t idx, int nv) {
+  F4 r;
+  if (BF16) {
+    const uint16_t* p = static_cast<const uint16_t*>(base) + idx;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) r.v[k] = k < nv ? bf16_widen(p[k]) : 0.0f;
+  } else {
+    const float* p = static_cast<const float*>(base) + idx;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) r.v[k] = k < nv ? p[k] : 0.0f;
+  }
+  return r;
+}
+
 // Streaming (nontemporal) variants for data touched once per step: the
 // whole-quad case uses the nontemporal hint, which on gfx950 lifts a pure
 // read stream from ~6.4 to ~7.1 TB/s; partial quads fall back to plain loads.

@@ -30,64 +30,152 @@ __device__ __forceinline__ double wave_fold(double v) {
   return v;
 }
 
-// SRC 0: e = |x|.  SRC 1: e = |beta1*m + omega1*g| (g fp32 or bf16 per GT).
-// One workgroup per block; it walks all W workers of that block, two at a
-// time (16 outstanding 16-byte loads per lane).
+// Lane sum of one worker over the block: acc = sum over the 4 rounds of
+// ((e0+e1)+(e2+e3)), e = |c| in fp64 (zero past the end of the tensor).
 template <int SRC, int GT>
-__global__ __launch_bounds__(kThreads) void k_m1_partial(M1Params p) {
-  __shared__ double sh_w[4][256];  // [wave][worker]
-  const BlockEnt be = p.blk[blockIdx.x];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int W = p.W;
-  constexpr int WB = 2;
-
-#pragma unroll 1
-  for (int i0 = 0; i0 < W; i0 += WB) {
-    F4 a[WB][kRounds], b[WB][kRounds];
+__device__ __forceinline__ double lane_sum(const M1Params& p, const F4 (&a)[kRounds],
+                                           const F4 (&b)[kRounds]) {
+  double acc = 0.0;
 #pragma unroll
-    for (int u = 0; u < WB; ++u) {
+  for (int r = 0; r < kRounds; ++r) {
+    double e[4];
 #pragma unroll
-      for (int r = 0; r < kRounds; ++r) {
-        const int loc = kThreads * kQuad * r + kQuad * tid;
-        const int nv = max(0, min(kQuad, be.len - loc));
-        const int64_t idx = static_cast<int64_t>(i0 + u) * p.ld + be.start + loc;
-        if (i0 + u < W && nv > 0) {
-          if (SRC == 0) {
-            a[u][r] = ldnt_f32x4(p.x + idx, nv);
-          } else {
-            a[u][r] = ldnt_f32x4(p.m + idx, nv);
-            b[u][r] = ldnt_x4<GT>(p.g, idx, nv);
-          }
-        } else {
-#pragma unroll
-          for (int k = 0; k < 4; ++k) a[u][r].v[k] = b[u][r].v[k] = 0.0f;
-        }
-      }
+    for (int k = 0; k < 4; ++k) {
+      float c;
+      if (SRC == 0) c = a[r].v[k];
+      else c = (p.beta1 * a[r].v[k]) + (p.omega1 * b[r].v[k]);
+      e[k] = fabs(static_cast<double>(c));
     }
+    acc = acc + ((e[0] + e[1]) + (e[2] + e[3]));
+  }
+  return acc;
+}
+
+// Loads of workers i0 .. i0+WB-1 for the thread's 4 quads (zeros for absent
+// workers and elements).
+template <int SRC, int GT, bool FULL, int WB>
+__device__ __forceinline__ void m1_load(const M1Params& p, const BlockEnt& be, int i0, int W,
+                                        const int (&nv)[kRounds], F4 (&a)[WB][kRounds],
+                                        F4 (&b)[WB][kRounds]) {
+  const int tid = threadIdx.x;
 #pragma unroll
-    for (int u = 0; u < WB; ++u) {
-      if (i0 + u >= W) break;
-      double acc = 0.0;
+  for (int u = 0; u < WB; ++u) {
 #pragma unroll
-      for (int r = 0; r < kRounds; ++r) {
-        double e[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          float c;
-          if (SRC == 0) c = a[u][r].v[k];
-          else c = (p.beta1 * a[u][r].v[k]) + (p.omega1 * b[u][r].v[k]);
-          e[k] = fabs(static_cast<double>(c));  // zero-filled past the end
+    for (int r = 0; r < kRounds; ++r) {
+      const int64_t idx = static_cast<int64_t>(i0 + u) * p.ld + be.start +
+                          (kThreads * kQuad * r + kQuad * tid);
+      if (FULL && i0 + u < W) {
+        if (SRC == 0) {
+          a[u][r] = ldnt_f32x4(p.x + idx, kQuad);
+        } else {
+          a[u][r] = ldnt_f32x4(p.m + idx, kQuad);
+          b[u][r] = ldnt_x4<GT>(p.g, idx, kQuad);
         }
-        acc = acc + ((e[0] + e[1]) + (e[2] + e[3]));
+      } else if (!FULL && i0 + u < W) {
+        const int n = nv[r];
+        if (SRC == 0) {
+          a[u][r] = ldm_f32x4(p.x + idx, n);
+        } else {
+          a[u][r] = ldm_f32x4(p.m + idx, n);
+          b[u][r] = ldm_x4<GT>(p.g, idx, n);
+        }
+      } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) a[u][r].v[k] = b[u][r].v[k] = 0.0f;
       }
-      acc = wave_fold(acc);
-      if (lane == 0) sh_w[wave][i0 + u] = acc;
     }
   }
+}
+
+// Fold NW (a power of two, 4..16) workers' lane sums at once.  A reduce-
+// scatter over the halving tree: at distance s, lane q keeps half of its
+// workers (the lower half if bit s of q is clear) and adds the partner's
+// value of the same worker, so each worker is still summed exactly as the
+// halving tree a[q] + a[q+s] (the mirrored lanes add the same pair, and IEEE
+// addition commutes).  After log2(NW) such steps each lane holds one worker;
+// the remaining distances fold it like wave_fold.  17 shuffles instead of 96
+// for 16 workers.  Returns the total of worker wk(lane) in `out`.
+template <int NW>
+__device__ __forceinline__ double fold_many(double (&v)[NW], int* wk) {
+  const int lane = threadIdx.x & 63;
+  int base = 0;
+  int n = NW;
+  int s = 32;
+#pragma unroll
+  for (int step = 0; (1 << step) < NW; ++step) {
+    const int h = n >> 1;
+    const bool upper = (lane & s) != 0;
+#pragma unroll
+    for (int k = 0; k < NW / 2; ++k) {
+      if (k >= h) break;
+      const double send = upper ? v[k] : v[k + h];
+      const double keep = upper ? v[k + h] : v[k];
+      const double recv = __shfl_xor(send, s, kWave);
+      v[k] = keep + recv;
+    }
+    if (upper) base += h;
+    n = h;
+    s >>= 1;
+  }
+  double r = v[0];
+  for (; s >= 1; s >>= 1) r = r + __shfl_xor(r, s, kWave);
+  *wk = base;
+  return r;
+}
+
+// SRC 0: e = |x|.  SRC 1: e = |beta1*m + omega1*g| (g fp32 or bf16 per GT).
+// One workgroup per block; it walks all W workers of that block, two at a
+// time (16 outstanding 16-byte loads per lane).  FULL blocks take straight
+// vector loads with no per-lane predicates; the ragged last block of a
+// tensor takes the masked path.  With WT = 4, 8 or 16 workers the lane sums
+// stay in registers and are folded together at the end (fold_many).
+template <int SRC, int GT, bool FULL, int WT>
+__device__ __forceinline__ void m1_block(const M1Params& p, const BlockEnt& be,
+                                         double (*sh_w)[256]) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int W = WT > 0 ? WT : p.W;
+  constexpr int WB = 2;  // workers per batch on the fixed-W path
+  int nv[kRounds];
+#pragma unroll
+  for (int r = 0; r < kRounds; ++r)
+    nv[r] = FULL ? kQuad : max(0, min(kQuad, be.len - (kThreads * kQuad * r + kQuad * tid)));
+
+  if constexpr (WT > 0) {
+    // fully unrolled over the fixed worker count: every index is static
+    double acc[WT];
+#pragma unroll
+    for (int i0 = 0; i0 < WT; i0 += WB) {
+      F4 a[WB][kRounds], b[WB][kRounds];
+      m1_load<SRC, GT, FULL, WB>(p, be, i0, W, nv, a, b);
+#pragma unroll
+      for (int u = 0; u < WB; ++u) acc[i0 + u] = lane_sum<SRC, GT>(p, a[u], b[u]);
+    }
+    int wk = 0;
+    const double tot = fold_many<WT>(acc, &wk);
+    if ((lane & (64 / WT - 1)) == 0) sh_w[wave][wk] = tot;
+  } else {
+    // generic W or a ragged block: one worker at a time, folded at once
+#pragma unroll 1
+    for (int i = 0; i < W; ++i) {
+      F4 a[1][kRounds], b[1][kRounds];
+      m1_load<SRC, GT, FULL, 1>(p, be, i, W, nv, a, b);
+      const double tot = wave_fold(lane_sum<SRC, GT>(p, a[0], b[0]));
+      if (lane == 0) sh_w[wave][i] = tot;
+    }
+  }
+}
+
+template <int SRC, int GT, int WT>
+__global__ __launch_bounds__(kThreads) void k_m1_partial(M1Params p) {
+  __shared__ double sh_w[4][256];  // [wave][worker]
+  const BlockEnt be = block_of(p.blk, p.flat, p.d);
+  const int tid = threadIdx.x;
+  if (be.len == kBlock) m1_block<SRC, GT, true, WT>(p, be, sh_w);
+  else m1_block<SRC, GT, false, 0>(p, be, sh_w);
   __syncthreads();
-  for (int i = tid; i < W; i += kThreads) {
+  for (int i = tid; i < p.W; i += kThreads) {
     const double P = (sh_w[0][i] + sh_w[1][i]) + (sh_w[2][i] + sh_w[3][i]);
-    p.partial[static_cast<int64_t>(i) * p.nblk + blockIdx.x] = P;
+    p.partial[static_cast<int64_t>(blockIdx.x) * p.W + i] = P;  // one run per block
   }
 }
 
@@ -100,7 +188,7 @@ __global__ __launch_bounds__(kThreads) void k_m1_group(M1Params p) {
   const int64_t gid = blockIdx.x;
   const int i = static_cast<int>(gid / p.ngrp), gg = static_cast<int>(gid % p.ngrp);
   const GroupEnt ge = p.grp[gg];
-  double v = tid < ge.cnt ? p.partial[static_cast<int64_t>(i) * p.nblk + ge.blk + tid] : 0.0;
+  double v = tid < ge.cnt ? p.partial[static_cast<int64_t>(ge.blk + tid) * p.W + i] : 0.0;
   v = wave_fold(v);
   if (lane == 0) sh[wave] = v;
   __syncthreads();
@@ -130,7 +218,7 @@ __global__ __launch_bounds__(kThreads) void k_m1_finalize(M1Params p) {
 
 // Eq. (1) codes of x: one workgroup per block, all workers.
 __global__ __launch_bounds__(kThreads) void k_quant_codes(M1Params p, int8_t* __restrict__ codes) {
-  const BlockEnt be = p.blk[blockIdx.x];
+  const BlockEnt be = block_of(p.blk, p.flat, p.d);
   const int tid = threadIdx.x;
   const double qm = static_cast<double>(p.qmax);
 #pragma unroll 1
@@ -155,11 +243,21 @@ __global__ __launch_bounds__(kThreads) void k_quant_codes(M1Params p, int8_t* __
   }
 }
 
+template <int SRC, int GT>
+static void launch_m1_t(const M1Params& p, hipStream_t st) {
+  const dim3 g(p.nblk), b(kThreads);
+  switch (p.W) {
+    case 4: hipLaunchKernelGGL((k_m1_partial<SRC, GT, 4>), g, b, 0, st, p); break;
+    case 8: hipLaunchKernelGGL((k_m1_partial<SRC, GT, 8>), g, b, 0, st, p); break;
+    case 16: hipLaunchKernelGGL((k_m1_partial<SRC, GT, 16>), g, b, 0, st, p); break;
+    default: hipLaunchKernelGGL((k_m1_partial<SRC, GT, 0>), g, b, 0, st, p); break;
+  }
+}
+
 hipError_t launch_m1(const M1Params& p, int src_x, int grad_bf16, hipStream_t st) {
-  const dim3 blk(kThreads);
-  if (src_x) hipLaunchKernelGGL((k_m1_partial<0, 0>), dim3(p.nblk), blk, 0, st, p);
-  else if (grad_bf16) hipLaunchKernelGGL((k_m1_partial<1, 1>), dim3(p.nblk), blk, 0, st, p);
-  else hipLaunchKernelGGL((k_m1_partial<1, 0>), dim3(p.nblk), blk, 0, st, p);
+  if (src_x) launch_m1_t<0, 0>(p, st);
+  else if (grad_bf16) launch_m1_t<1, 1>(p, st);
+  else launch_m1_t<1, 0>(p, st);
   return hipGetLastError();
 }
 

@@ -56,6 +56,9 @@ struct StepParams {
   int32_t avg_step;    // t % sync_every == 0
   int32_t tie_zero;
   int32_t qmax;
+  int32_t flat;        // one tensor: block b starts at b*kBlock (no table load)
+  int32_t any_sync;    // some tensor is averaged (else no tensor-table load)
+  int64_t d;
   // optional outputs
   uint64_t* bits;
   int8_t* codes;
@@ -71,7 +74,7 @@ struct M1Params {
   const float* m;      // [W][ld] with
   const void* g;       // [W][ld]: c = beta1*m + omega1*g
   const GroupEnt* grp;
-  double* partial;     // [W][nblk]
+  double* partial;     // [nblk][W]: each block's W partials written as one run
   double* gval;        // [W][ngrp]
   double* m1;          // [W][nT]
   double* scale;       // [W][nT]
@@ -82,7 +85,22 @@ struct M1Params {
   int32_t nblk;
   int32_t ngrp;
   int32_t qmax;
+  int32_t flat;        // one tensor: block b starts at b*kBlock (no table load)
+  int64_t d;
   float beta1, omega1;
 };
+
+// Block b's descriptor; a single-tensor vector needs no table load.
+__device__ __forceinline__ BlockEnt block_of(const BlockEnt* blk, int flat, int64_t d) {
+  if (flat) {
+    BlockEnt be;
+    be.start = static_cast<int64_t>(blockIdx.x) * kBlock;
+    const int64_t rem = d - be.start;
+    be.len = static_cast<int32_t>(rem < kBlock ? rem : kBlock);
+    be.tensor = 0;
+    return be;
+  }
+  return blk[blockIdx.x];
+}
 
 }  // namespace lioncub

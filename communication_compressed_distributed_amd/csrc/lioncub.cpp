@@ -102,6 +102,7 @@ struct lioncub_ctx {
   hipStream_t stream;
   int32_t nblk;
   int32_t ngrp;
+  int32_t any_sync;
   BlockEnt* blk;
   TensorEnt* tens;
   GroupEnt* grp;
@@ -152,6 +153,9 @@ void fill_step_params(const lioncub_ctx* c, StepParams* p) {
   p->lr = c->cfg.lr;
   p->wd = c->cfg.wd;
   p->tie_zero = c->cfg.tie_mode == LIONCUB_TIE_ZERO;
+  p->flat = c->cfg.n_tensors == 1;
+  p->any_sync = c->any_sync;
+  p->d = c->cfg.d;
   p->qmax = c->cfg.qbits >= 2 ? (1 << (c->cfg.qbits - 1)) - 1 : 0;
 }
 
@@ -172,6 +176,8 @@ void fill_m1_params(const lioncub_ctx* c, M1Params* p) {
   p->qmax = c->cfg.qbits >= 2 && c->cfg.qbits <= 8 ? (1 << (c->cfg.qbits - 1)) - 1 : 0;
   p->beta1 = c->cfg.beta1;
   p->omega1 = 1.0f - c->cfg.beta1;
+  p->flat = c->cfg.n_tensors == 1;
+  p->d = c->cfg.d;
 }
 
 int dev_status(hipError_t e) { return e == hipSuccess ? LIONCUB_OK : LIONCUB_EDEVICE; }
@@ -224,6 +230,7 @@ int lioncub_init(lioncub_ctx** out, const lioncub_config* cfg, void* hip_stream,
     te.grp0 = static_cast<int32_t>(c->h_grp.size());
     te.ngrp = (te.nblk + kGroup - 1) / kGroup;
     te.sync = cfg->sync_m ? (cfg->sync_m[T] ? 1 : 0) : 0;
+    c->any_sync |= te.sync;
     te.pad = 0;
     for (int32_t gq = 0; gq < te.ngrp; ++gq) {
       GroupEnt ge;

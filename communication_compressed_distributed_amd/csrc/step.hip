@@ -69,9 +69,24 @@ __device__ __forceinline__ void step_block(const StepParams& p, const BlockEnt& 
     for (int k = 0; k < 4; ++k) sum[q][k] = 0;
   }
 
+  // The W scales of this tensor (L1 path) are staged in LDS once per block:
+  // a vector load after the batch's data loads would make every wave wait
+  // for all of them before its first product; an LDS read is counted apart
+  // from the memory loads and arrives first.
+  __shared__ double sh_sc[256];
+  if (AGG == 1) {
+    for (int i = tid; i < W; i += kThreads) sh_sc[i] = scl[static_cast<int64_t>(i) * p.nT];
+    __syncthreads();
+  }
+
   constexpr bool kExact = WT > 0 && WT % WB == 0;
 #pragma unroll 1
   for (int i0 = 0; i0 < W; i0 += WB) {
+    double sc_b[WB];
+    if (AGG == 1) {
+#pragma unroll
+      for (int b = 0; b < WB; ++b) sc_b[b] = (kExact || i0 + b < W) ? sh_sc[i0 + b] : 0.0;
+    }
     F4 mv[WB][Q], gv[WB][Q];
 #pragma unroll
     for (int b = 0; b < WB; ++b) {
@@ -91,8 +106,7 @@ __device__ __forceinline__ void step_block(const StepParams& p, const BlockEnt& 
     for (int b = 0; b < WB; ++b) {
       const int i = i0 + b;
       if (!kExact && i >= W) break;
-      double s_i = 0.0;
-      if (AGG == 1) s_i = scl[static_cast<int64_t>(i) * p.nT];
+      const double s_i = AGG == 1 ? sc_b[b] : 0.0;
 #pragma unroll
       for (int q = 0; q < Q; ++q) {
         const int64_t idx = static_cast<int64_t>(i) * p.ld + j[q];
@@ -181,8 +195,8 @@ __device__ __forceinline__ void step_block(const StepParams& p, const BlockEnt& 
 
 template <int TT, int GT, bool DBG, int AGG, int WB, int WT>
 __global__ __launch_bounds__(kThreads) void k_step(StepParams p) {
-  const BlockEnt be = p.blk[blockIdx.x];
-  const bool avg = p.avg_step && p.tens[be.tensor].sync;
+  const BlockEnt be = block_of(p.blk, p.flat, p.d);
+  const bool avg = p.avg_step && p.any_sync && p.tens[be.tensor].sync;
   const uint32_t par = static_cast<uint32_t>(p.parity);
   if (be.len == kBlock) {
     if (avg) step_block<TT, GT, DBG, AGG, WB, WT, true, true>(p, be, par);
