@@ -269,7 +269,7 @@ void lco_step_range(const lco_cfg *cfg, int64_t j0, int64_t j1,
     for (int32_t i = 0; i < W; i++) {
       float G = load_g(cfg, g, i * ldc + col);
       float c = (cfg->beta1 * m[i * ldc + col]) + (omega1 * G);
-      if (cfg->agg == LCO_AGG_VOTE) {
+      if (cfg->agg != LCO_AGG_L1SUM) {
         int b = lco_bit(c, t);
         count += b;
         if (dbg && dbg->bits && b)
@@ -281,19 +281,29 @@ void lco_step_range(const lco_cfg *cfg, int64_t j0, int64_t j1,
       }
     }
     int8_t s;
+    float sf;
     if (cfg->agg == LCO_AGG_VOTE) {
       s = vote_sign(W, count, t, cfg->tie_mode);
+      sf = (float)s;
+    } else if (cfg->agg == LCO_AGG_AVG) {
+      /* [DL] "Approach": the server averages the workers' binary update
+       * vectors, so the applied update is the mean of the W signs,
+       * (count*(+1) + (W-count)*(-1)) / W, one fp32 division; the int8
+       * sign output records its sign. */
+      int32_t net = 2 * count - W;
+      sf = (float)net / (float)W;
+      s = (int8_t)((net > 0) - (net < 0));
     } else {
       /* [LC]: a global sign of the integer sum; the p-bit sum can carry
        * zero, so sgn(0) = 0 and the parameter only decays. */
       s = (int8_t)((sum > 0) - (sum < 0));
+      sf = (float)s;
     }
     if (dbg && dbg->counts) dbg->counts[col] = (uint8_t)count;
     if (dbg && dbg->sums) dbg->sums[col] = sum;
     if (dbg && dbg->sign) dbg->sign[col] = s;
 
     /* 4: theta <- theta - lr*(sign + wd*theta) */
-    float sf = (float)s;
     if (cfg->theta_bf16) {
       uint16_t *th = (uint16_t *)theta;
       float x = lco_bf16_to_f32(th[col]);
@@ -316,6 +326,100 @@ void lco_step_range(const lco_cfg *cfg, int64_t j0, int64_t j1,
       float avg = acc / (float)W;
       for (int32_t i = 0; i < W; i++) m[i * ldc + col] = avg;
     }
+  }
+}
+
+/* ------------------- receive side and wire formats of the exchange ---- */
+
+/* [LC] the 1-bit path: after the AlltoAll each worker votes on its slice and
+ * the 1-bit result is all-gathered; a 2-bit result can also carry zero. */
+void lco_vote_bits(int32_t W, int64_t d, int64_t ld, const uint64_t *bits,
+                   int64_t t, int32_t tie_mode, uint64_t *sign_bits,
+                   uint64_t *zero_bits) {
+  int64_t words = ld / 64;
+  for (int64_t k = 0; k < words; k++) {
+    sign_bits[k] = 0;
+    if (zero_bits) zero_bits[k] = 0;
+  }
+  for (int64_t j = 0; j < d; j++) {
+    int32_t v = 0;
+    for (int32_t i = 0; i < W; i++)
+      v += (int32_t)((bits[i * words + j / 64] >> (j % 64)) & 1u);
+    int8_t s = vote_sign(W, v, t, tie_mode);
+    if (s > 0) sign_bits[j / 64] |= (uint64_t)1 << (j % 64);
+    if (s == 0 && zero_bits) zero_bits[j / 64] |= (uint64_t)1 << (j % 64);
+  }
+}
+
+void lco_apply(const lco_cfg *cfg, int64_t ld, void *theta, float *m,
+               const void *g, int64_t t, const uint64_t *sign_bits,
+               const uint64_t *zero_bits) {
+  const int32_t W = cfg->W;
+  const float omega2 = 1.0f - cfg->beta2;
+  const int avg_step = (t % cfg->sync_every) == 0;
+  int32_t T = 0;
+  for (int64_t j = 0; j < cfg->d; j++) {
+    while (T + 1 < cfg->n_tensors && cfg->off[T + 1] <= j) T++;
+    int pos = (int)((sign_bits[j / 64] >> (j % 64)) & 1u);
+    int zer = zero_bits ? (int)((zero_bits[j / 64] >> (j % 64)) & 1u) : 0;
+    float sf = zer ? 0.0f : (pos ? 1.0f : -1.0f);
+    if (cfg->theta_bf16) {
+      uint16_t *th = (uint16_t *)theta;
+      float x = lco_bf16_to_f32(th[j]);
+      th[j] = lco_f32_to_bf16(x - (cfg->lr * (sf + (cfg->wd * x))));
+    } else {
+      float *th = (float *)theta;
+      float x = th[j];
+      th[j] = x - (cfg->lr * (sf + (cfg->wd * x)));
+    }
+    for (int32_t i = 0; i < W; i++) {
+      float G = load_g(cfg, g, i * ld + j);
+      m[i * ld + j] = (cfg->beta2 * m[i * ld + j]) + (omega2 * G);
+    }
+    if (avg_step && cfg->sync_m && cfg->sync_m[T]) {
+      float acc = m[j];
+      for (int32_t i = 1; i < W; i++) acc = acc + m[i * ld + j];
+      float avg = acc / (float)W;
+      for (int32_t i = 0; i < W; i++) m[i * ld + j] = avg;
+    }
+  }
+}
+
+/* [LC] the p-bit path sends Eq. (1) codes in n bits each (Figure 1: 1-bit
+ * vs p-bit allreduce); the sum needs more bits than one code (the referee
+ * report's note that a uint8 only fits 0/1 sums), hence int32 here. */
+void lco_pack_codes(int32_t W, int64_t d, int64_t ld, int32_t qbits,
+                    const int8_t *codes, uint32_t *wire) {
+  int64_t wpr = (ld / 32) * qbits;
+  uint32_t mask = (1u << qbits) - 1u;
+  for (int32_t i = 0; i < W; i++) {
+    for (int64_t k = 0; k < wpr; k++) wire[i * wpr + k] = 0;
+    for (int64_t j = 0; j < d; j++) {
+      uint32_t field = (uint32_t)(int32_t)codes[i * ld + j] & mask;
+      int64_t bit = (j / 32) * 32 * qbits + (j % 32) * qbits;  /* bit offset in row */
+      for (int32_t b = 0; b < qbits; b++)
+        if ((field >> b) & 1u)
+          wire[i * wpr + (bit + b) / 32] |= 1u << ((bit + b) % 32);
+    }
+  }
+}
+
+void lco_unpack_sum(int32_t W, int64_t d, int64_t ld, int32_t qbits,
+                    const uint32_t *wire, int32_t *sums, int8_t *sign) {
+  int64_t wpr = (ld / 32) * qbits;
+  for (int64_t j = 0; j < d; j++) {
+    int32_t S = 0;
+    int64_t bit = (j / 32) * 32 * qbits + (j % 32) * qbits;
+    for (int32_t i = 0; i < W; i++) {
+      uint32_t field = 0;
+      for (int32_t b = 0; b < qbits; b++)
+        field |= ((wire[i * wpr + (bit + b) / 32] >> ((bit + b) % 32)) & 1u) << b;
+      int32_t q = (field & (1u << (qbits - 1))) ? (int32_t)field - (1 << qbits)
+                                                 : (int32_t)field;
+      S += q;
+    }
+    if (sums) sums[j] = S;
+    if (sign) sign[j] = (int8_t)((S > 0) - (S < 0));
   }
 }
 

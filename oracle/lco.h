@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-enum { LCO_AGG_VOTE = 0, LCO_AGG_L1SUM = 1 };
+enum { LCO_AGG_VOTE = 0, LCO_AGG_L1SUM = 1, LCO_AGG_AVG = 2 };
 enum { LCO_TIE_PARITY = 0, LCO_TIE_ZERO = 1 };
 
 /* Block / lane constants of the fixed mean-|x| summation tree (D-M1). */
@@ -53,7 +53,7 @@ typedef struct {
   int32_t sync_every;      /* averaging on steps with t % sync_every == 0  */
   int32_t theta_bf16;      /* theta stored as bf16 (else fp32)             */
   int32_t grad_bf16;       /* g stored as bf16 (else fp32)                 */
-  int32_t agg;             /* LCO_AGG_VOTE or LCO_AGG_L1SUM                */
+  int32_t agg;             /* LCO_AGG_VOTE, LCO_AGG_L1SUM or LCO_AGG_AVG   */
   int32_t qbits;           /* n of Eq. (1), 2..8, L1 path only             */
   int32_t tie_mode;        /* LCO_TIE_PARITY or LCO_TIE_ZERO, vote path    */
   float beta1, beta2, lr, wd;
@@ -130,6 +130,36 @@ typedef struct {
 void lco_step_range(const lco_cfg *cfg, int64_t j0, int64_t j1,
                     const double *m1, void *theta, float *m, const void *g,
                     int64_t ldc, int64_t t, const lco_debug *dbg);
+
+/* ---- receive side and wire formats of the worker-sharded exchange ---- */
+
+/* Global sign of the majority vote as bit planes: sign_bits[ld/64] has bit
+ * 1 where the sign is +1; zero_bits[ld/64] (may be NULL) has bit 1 where it
+ * is 0 (ties under LCO_TIE_ZERO).  Under LCO_TIE_PARITY a tie is carried by
+ * the parity bit, as a 1-bit all-gather would carry it.  Bits past d are 0. */
+void lco_vote_bits(int32_t W, int64_t d, int64_t ld, const uint64_t *bits,
+                   int64_t t, int32_t tie_mode, uint64_t *sign_bits,
+                   uint64_t *zero_bits);
+
+/* Apply a global sign given as bit planes (zero_bits may be NULL: no zeros):
+ * theta <- theta - lr*(s + wd*theta), then every worker's momentum update and
+ * the selective averaging, exactly as steps 4-5 of lco_step. */
+void lco_apply(const lco_cfg *cfg, int64_t ld, void *theta, float *m,
+               const void *g, int64_t t, const uint64_t *sign_bits,
+               const uint64_t *zero_bits);
+
+/* n-bit wire packing of Eq. (1) codes: per worker row, every 32 elements
+ * form one group of n 32-bit words; element k of a group occupies bits
+ * n*k .. n*k+n-1 of the group's little-endian bit string, as an n-bit two's
+ * complement integer.  Row stride (ld/32)*n words; elements past d are 0. */
+void lco_pack_codes(int32_t W, int64_t d, int64_t ld, int32_t qbits,
+                    const int8_t *codes, uint32_t *wire);
+
+/* Receive side of the p-bit exchange: unpack every worker's codes of each
+ * element, sum them in int32 and take the sign (sgn(0) = 0).  Either output
+ * may be NULL. */
+void lco_unpack_sum(int32_t W, int64_t d, int64_t ld, int32_t qbits,
+                    const uint32_t *wire, int32_t *sums, int8_t *sign);
 
 /* One whole step in place on the full state (theta[d], m[W][ld], g[W][ld]). */
 void lco_step(const lco_cfg *cfg, int64_t ld, void *theta, float *m,

@@ -11,7 +11,7 @@ import numpy as np
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "liblco.so")
 
-VOTE, L1SUM = 0, 1
+VOTE, L1SUM, AVG = 0, 1, 2
 TIE_PARITY, TIE_ZERO = 0, 1
 M1_BLOCK = 4096
 
@@ -65,6 +65,10 @@ def lib():
         L.lco_step_range.argtypes = [C.POINTER(Cfg), i64, i64, vp, vp, vp, vp, i64, i64,
                                      C.POINTER(Debug)]
         L.lco_step.argtypes = [C.POINTER(Cfg), i64, vp, vp, vp, i64, C.POINTER(Debug)]
+        L.lco_vote_bits.argtypes = [i32, i64, i64, vp, i64, i32, vp, vp]
+        L.lco_apply.argtypes = [C.POINTER(Cfg), i64, vp, vp, vp, i64, vp, vp]
+        L.lco_pack_codes.argtypes = [i32, i64, i64, i32, vp, vp]
+        L.lco_unpack_sum.argtypes = [i32, i64, i64, i32, vp, vp, vp]
         _lib = L
     return _lib
 
@@ -92,7 +96,7 @@ class OracleCfg:
         c.sync_every = wl.sync_every
         c.theta_bf16 = 1 if wl.theta_dtype == "bf16" else 0
         c.grad_bf16 = 1 if wl.grad_dtype == "bf16" else 0
-        c.agg = L1SUM if wl.agg == "l1" else VOTE
+        c.agg = {"l1": L1SUM, "avg": AVG}.get(wl.agg, VOTE)
         c.qbits = wl.qbits
         c.tie_mode = TIE_ZERO if wl.tie == "zero" else TIE_PARITY
         c.beta1, c.beta2, c.lr, c.wd = wl.beta1, wl.beta2, wl.lr, wl.wd
@@ -229,3 +233,38 @@ def step_range(wl, j0, j1, m1v, theta_c, m_c, g_c, t, debug=False):
     lib().lco_step_range(cfg.ref, j0, j1, _p(m1p), _p(theta_c), _p(m_c), _p(g_c), ldc, t,
                          C.byref(dbg) if dbg is not None else None)
     return arr
+
+
+def vote_bits(bits, W, d, t, tie_mode=TIE_PARITY, zero=True):
+    """-> (sign_bits[ld/64], zero_bits[ld/64] or None) uint64."""
+    bits = np.ascontiguousarray(bits, dtype=np.uint64)
+    words = bits.shape[1]
+    sb = np.empty(words, dtype=np.uint64)
+    zb = np.empty(words, dtype=np.uint64) if zero else None
+    lib().lco_vote_bits(W, d, words * 64, _p(bits), t, tie_mode, _p(sb), _p(zb))
+    return sb, zb
+
+
+def apply(wl, theta, m, g, t, sign_bits, zero_bits=None):
+    """Steps 4-5 from a global sign given as bit planes, in place."""
+    cfg = OracleCfg(wl)
+    lib().lco_apply(cfg.ref, m.shape[1], _p(theta), _p(m), _p(g), t,
+                    _p(np.ascontiguousarray(sign_bits, dtype=np.uint64)),
+                    _p(None if zero_bits is None else np.ascontiguousarray(zero_bits, np.uint64)))
+
+
+def pack_codes(codes, d, qbits):
+    """codes[W][ld] int8 -> wire[W][(ld/32)*qbits] uint32."""
+    codes = np.ascontiguousarray(codes, dtype=np.int8)
+    W, ld = codes.shape
+    wire = np.empty((W, (ld // 32) * qbits), dtype=np.uint32)
+    lib().lco_pack_codes(W, d, ld, qbits, _p(codes), _p(wire))
+    return wire
+
+
+def unpack_sum(wire, W, d, ld, qbits):
+    wire = np.ascontiguousarray(wire, dtype=np.uint32)
+    sums = np.empty(d, dtype=np.int32)
+    sign = np.empty(d, dtype=np.int8)
+    lib().lco_unpack_sum(W, d, ld, qbits, _p(wire), _p(sums), _p(sign))
+    return sums, sign

@@ -502,3 +502,117 @@ def test_chunked_step_equals_whole_step(oracle, agg):
         m_2[:, j0:j1] = mc
     assert np.array_equal(th1, th2)
     assert np.array_equal(m_1, m_2)
+
+
+# ------------------------- receive side and wire formats (worker-sharded) --
+
+def _words_to_bits(w, n):
+    return np.unpackbits(np.ascontiguousarray(w).view(np.uint8), bitorder="little")[:n]
+
+
+@pytest.mark.parametrize("W", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("tie", ["parity", "zero"])
+def test_vote_bits_decode_to_vote_sign(oracle, W, tie):
+    """The global-sign bit planes decode (zero ? 0 : sign ? +1 : -1) to the
+    brute-force-pinned vote sign for every sign pattern, both parities; a
+    parity tie sets no zero bit (a 1-bit result carries it); NumPy's
+    unpackbits reads the planes."""
+    tm = oracle.TIE_ZERO if tie == "zero" else oracle.TIE_PARITY
+    pats = np.array(list(itertools.product([-1.0, 0.0, 1.0], repeat=W)), dtype=np.float32)
+    for t in (1, 2):
+        for a in range(0, len(pats), 64):
+            chunk = pats[a:a + 64]
+            d = len(chunk)
+            x = np.zeros((W, 64), dtype=np.float32)
+            x[:, :d] = chunk.T
+            bits = oracle.pack(x, d, t)
+            _, sign = oracle.vote(bits, W, d, t, tm)
+            sb, zb = oracle.vote_bits(bits, W, d, t, tm)
+            pos = _words_to_bits(sb, 64)
+            zer = _words_to_bits(zb, 64)
+            dec = np.where(zer[:d] == 1, 0, np.where(pos[:d] == 1, 1, -1))
+            assert np.array_equal(dec, sign)
+            assert not pos[d:].any() and not zer[d:].any()
+            if tm == oracle.TIE_PARITY:
+                assert not zer.any()
+
+
+def test_apply_closed_form(oracle):
+    """A constant global sign s applied T times: theta_T = a^T theta_0 -
+    s (1 - a^T) / wd (s = 0: pure decay a^T theta_0), m_T = (1 - b2^T) g
+    from m_0 = 0, independent of the sign."""
+    W, d = 3, 256
+    wl = wls.flat("ap", d, W=W)
+    rs = np.random.default_rng(12)
+    theta0 = rs.normal(0, 0.05, d).astype(np.float32)
+    theta = theta0.copy()
+    m = np.zeros((W, d), np.float32)
+    g = rs.normal(0, 1e-2, (W, d)).astype(np.float32)
+    s = rs.integers(-1, 2, d)
+    sb = np.packbits(s > 0, bitorder="little").view("<u8").copy()
+    zb = np.packbits(s == 0, bitorder="little").view("<u8").copy()
+    T = 8
+    for t in range(1, T + 1):
+        oracle.apply(wl, theta, m, g, t, sb, zb)
+    lr, wd, b2 = float(np.float32(1e-4)), float(np.float32(0.1)), float(np.float32(0.99))
+    a = 1 - lr * wd
+    want = a**T * theta0.astype(np.float64) - s * (1 - a**T) / wd
+    np.testing.assert_allclose(theta, want, rtol=2e-6, atol=1e-10)
+    np.testing.assert_allclose(m, (1 - b2**T) * g.astype(np.float64), rtol=2e-6)
+
+
+def test_pack_codes_handworked(oracle):
+    """n = 4: codes [1, -1, 7, -7, 0, 3] are the nibbles 1, F, 7, 9, 0, 3 from
+    the least significant end: word 0x003097F1.  n = 3: element 10 occupies
+    bits 30..32 and straddles words 0 and 1; code -3 is 0b101 (bits 30, 32)."""
+    c = np.zeros((1, 64), np.int8)
+    c[0, :6] = [1, -1, 7, -7, 0, 3]
+    w = oracle.pack_codes(c, 6, 4)
+    assert w.shape == (1, 8) and int(w[0, 0]) == 0x003097F1 and not w[0, 1:].any()
+    c = np.zeros((1, 64), np.int8)
+    c[0, 10] = -3
+    w = oracle.pack_codes(c, 11, 3)
+    assert int(w[0, 0]) == 1 << 30 and int(w[0, 1]) == 1 and not w[0, 2:].any()
+
+
+@pytest.mark.parametrize("n", [2, 3, 4, 5, 7, 8])
+def test_pack_codes_roundtrip_and_sum(oracle, n):
+    """Independent decode with NumPy (unpackbits, n-bit two's complement)
+    recovers the codes; unpack_sum equals NumPy's column sums."""
+    qmax = 2 ** (n - 1) - 1
+    rs = np.random.default_rng(n)
+    W, d = 5, 1000
+    ld = 1024
+    codes = np.zeros((W, ld), np.int8)
+    codes[:, :d] = rs.integers(-qmax, qmax + 1, (W, d))
+    wire = oracle.pack_codes(codes, d, n)
+    assert wire.shape == (W, (ld // 32) * n)
+    bits = np.unpackbits(wire.view(np.uint8), axis=1, bitorder="little")
+    fields = bits.reshape(W, ld // 32, 32, n)           # group, element, bit
+    val = (fields * (1 << np.arange(n))).sum(axis=3).reshape(W, ld)
+    val = np.where(val >= 1 << (n - 1), val - (1 << n), val)
+    assert np.array_equal(val[:, :d], codes[:, :d]) and not val[:, d:].any()
+    sums, sign = oracle.unpack_sum(wire, W, d, ld, n)
+    assert np.array_equal(sums, codes[:, :d].astype(np.int32).sum(axis=0))
+    assert np.array_equal(sign, np.sign(sums).astype(np.int8))
+
+
+def test_avg_aggregation_values(oracle):
+    """D-Lion averaging: the applied update is the mean of the W signs,
+    (2v - W)/W correctly rounded to fp32 (Python's Fraction -> float rounds
+    correctly; fp32 via NumPy), e.g. 1/3 -> 0.33333334 for W = 3, v = 2.
+    With identical workers it is plain Lion (s = +-1, the closed form)."""
+    for W in (3, 4, 7):
+        pats = np.array(list(itertools.product([-1.0, 1.0], repeat=W)), dtype=np.float32)
+        d = len(pats)
+        wl = wls.flat("avg", d, W=W, agg="avg", beta1=0.5, lr=1.0, wd=0.0)
+        theta = np.zeros(d, np.float32)
+        m = np.zeros((W, wl.ld), np.float32)
+        g = np.zeros((W, wl.ld), np.float32)
+        g[:, :d] = pats.T * 2                      # c = g/2 exactly
+        dbg = oracle.step(wl, theta, m, g, 1, debug=True)
+        v = (pats > 0).sum(axis=1)
+        want = np.array([np.float32(float(Fraction(int(2 * k - W), W))) for k in v])
+        assert np.array_equal(theta, -want)        # theta' = 0 - 1*(s + 0)
+        assert np.array_equal(dbg["sign"], np.sign(2 * v - W).astype(np.int8))
+    assert np.float32(float(Fraction(1, 3))) == np.float32(0.33333334)
