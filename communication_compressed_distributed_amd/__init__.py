@@ -8,16 +8,19 @@ sign updates the parameters and each worker's momentum.  `_abi` mirrors the C
 entry points; `LionCub` keeps a context and its workspace together.
 """
 from . import _abi
-from ._abi import (AGG_L1SUM, AGG_VOTE, BF16, F32, TIE_PARITY, TIE_ZERO, LionCubError,
-                   lioncub_destroy, lioncub_init, lioncub_pack, lioncub_profile_begin,
-                   lioncub_profile_end, lioncub_quant_l1, lioncub_set_stream, lioncub_step,
-                   lioncub_strerror, lioncub_vote, lioncub_workspace_bytes, make_config)
+from ._abi import (AGG_AVG, AGG_L1SUM, AGG_VOTE, BF16, F32, TIE_PARITY, TIE_ZERO, LionCubError,
+                   lioncub_apply, lioncub_destroy, lioncub_init, lioncub_pack,
+                   lioncub_pack_codes, lioncub_profile_begin, lioncub_profile_end,
+                   lioncub_quant_l1, lioncub_set_stream, lioncub_step, lioncub_strerror,
+                   lioncub_unpack_sum, lioncub_vote, lioncub_vote_bits, lioncub_workspace_bytes,
+                   make_config)
 
 __all__ = ["LionCub", "LionCubError", "make_config", "lioncub_workspace_bytes", "lioncub_init",
            "lioncub_set_stream", "lioncub_step", "lioncub_pack", "lioncub_vote",
-           "lioncub_quant_l1", "lioncub_profile_begin", "lioncub_profile_end",
+           "lioncub_quant_l1", "lioncub_vote_bits", "lioncub_apply", "lioncub_pack_codes",
+           "lioncub_unpack_sum", "lioncub_profile_begin", "lioncub_profile_end",
            "lioncub_destroy", "lioncub_strerror", "F32", "BF16", "AGG_VOTE", "AGG_L1SUM",
-           "TIE_PARITY", "TIE_ZERO"]
+           "AGG_AVG", "TIE_PARITY", "TIE_ZERO"]
 
 
 class LionCub:
@@ -36,7 +39,7 @@ class LionCub:
             d, ld, W, offs, sync_m=sync_m, sync_every=sync_every,
             theta_dtype=BF16 if theta_dtype == "bf16" else F32,
             grad_dtype=BF16 if grad_dtype == "bf16" else F32,
-            agg=AGG_L1SUM if agg == "l1" else AGG_VOTE, qbits=qbits,
+            agg={"l1": AGG_L1SUM, "avg": AGG_AVG}.get(agg, AGG_VOTE), qbits=qbits,
             tie_mode=TIE_ZERO if tie == "zero" else TIE_PARITY,
             beta1=beta1, beta2=beta2, lr=lr, wd=wd)
         self.d, self.ld, self.W, self.n_tensors = d, ld, W, len(offs) - 1
@@ -58,6 +61,18 @@ class LionCub:
 
     def quant_l1(self, x, codes, m1=None):
         lioncub_quant_l1(self.ctx, x, codes, m1)
+
+    def vote_bits(self, bits, t, sign_bits, zero_bits=None):
+        lioncub_vote_bits(self.ctx, bits, t, sign_bits, zero_bits)
+
+    def apply(self, theta, m, g, t, sign_bits, zero_bits=None):
+        lioncub_apply(self.ctx, theta, m, g, t, sign_bits, zero_bits)
+
+    def pack_codes(self, codes, wire):
+        lioncub_pack_codes(self.ctx, codes, wire)
+
+    def unpack_sum(self, wire, sums=None, sign=None):
+        lioncub_unpack_sum(self.ctx, wire, sums, sign)
 
     def profile_begin(self, capacity):
         lioncub_profile_begin(self.ctx, capacity)

@@ -14,13 +14,16 @@ LIB_PATH = os.path.join(HERE, "liblioncub.so")
 
 OK, EINVAL, EALIGN, EWORKSPACE, EDEVICE, EUNSUPPORTED = 0, -1, -2, -3, -4, -5
 F32, BF16 = 0, 1
-AGG_VOTE, AGG_L1SUM = 0, 1
+AGG_VOTE, AGG_L1SUM, AGG_AVG = 0, 1, 2
 TIE_PARITY, TIE_ZERO = 0, 1
-K_VOTE_STEP, K_M1_PARTIAL, K_M1_FINALIZE, K_L1_STEP, K_PACK, K_VOTE, K_QUANT, K_COUNT = range(8)
-KERNEL_NAMES = ["vote_step", "m1_partial", "m1_finalize", "l1_step", "pack", "vote", "quant"]
+(K_VOTE_STEP, K_M1_PARTIAL, K_M1_FINALIZE, K_L1_STEP, K_PACK, K_VOTE, K_QUANT, K_VOTE_BITS,
+ K_APPLY, K_PACK_CODES, K_UNPACK_SUM, K_AVG_STEP, K_COUNT) = range(13)
+KERNEL_NAMES = ["vote_step", "m1_partial", "m1_finalize", "l1_step", "pack", "vote", "quant",
+                "vote_bits", "apply", "pack_codes", "unpack_sum", "avg_step"]
 
 EXPORTS = ["lioncub_workspace_bytes", "lioncub_init", "lioncub_set_stream", "lioncub_step",
-           "lioncub_pack", "lioncub_vote", "lioncub_quant_l1", "lioncub_profile_begin",
+           "lioncub_pack", "lioncub_vote", "lioncub_quant_l1", "lioncub_vote_bits",
+           "lioncub_apply", "lioncub_pack_codes", "lioncub_unpack_sum", "lioncub_profile_begin",
            "lioncub_profile_end", "lioncub_destroy", "lioncub_strerror"]
 
 
@@ -65,6 +68,14 @@ def lib():
         L.lioncub_vote.restype = C.c_int
         L.lioncub_quant_l1.argtypes = [vp, vp, vp, vp]
         L.lioncub_quant_l1.restype = C.c_int
+        L.lioncub_vote_bits.argtypes = [vp, vp, i64, vp, vp]
+        L.lioncub_vote_bits.restype = C.c_int
+        L.lioncub_apply.argtypes = [vp, vp, vp, vp, i64, vp, vp]
+        L.lioncub_apply.restype = C.c_int
+        L.lioncub_pack_codes.argtypes = [vp, vp, vp]
+        L.lioncub_pack_codes.restype = C.c_int
+        L.lioncub_unpack_sum.argtypes = [vp, vp, vp, vp]
+        L.lioncub_unpack_sum.restype = C.c_int
         L.lioncub_profile_begin.argtypes = [vp, i32]
         L.lioncub_profile_begin.restype = C.c_int
         L.lioncub_profile_end.argtypes = [vp, C.POINTER(C.c_double), C.POINTER(C.c_int32)]
@@ -155,6 +166,24 @@ def lioncub_vote(ctx, bits, t, counts=None, sign=None):
 
 def lioncub_quant_l1(ctx, x, codes, m1=None):
     _check("lioncub_quant_l1", lib().lioncub_quant_l1(ctx, _ptr(x), _ptr(codes), _ptr(m1)))
+
+
+def lioncub_vote_bits(ctx, bits, t, sign_bits, zero_bits=None):
+    _check("lioncub_vote_bits", lib().lioncub_vote_bits(ctx, _ptr(bits), int(t), _ptr(sign_bits),
+                                                        _ptr(zero_bits)))
+
+
+def lioncub_apply(ctx, theta, m, g, t, sign_bits, zero_bits=None):
+    _check("lioncub_apply", lib().lioncub_apply(ctx, _ptr(theta), _ptr(m), _ptr(g), int(t),
+                                                _ptr(sign_bits), _ptr(zero_bits)))
+
+
+def lioncub_pack_codes(ctx, codes, wire):
+    _check("lioncub_pack_codes", lib().lioncub_pack_codes(ctx, _ptr(codes), _ptr(wire)))
+
+
+def lioncub_unpack_sum(ctx, wire, sums=None, sign=None):
+    _check("lioncub_unpack_sum", lib().lioncub_unpack_sum(ctx, _ptr(wire), _ptr(sums), _ptr(sign)))
 
 
 def lioncub_profile_begin(ctx, capacity):

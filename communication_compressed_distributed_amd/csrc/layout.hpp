@@ -59,6 +59,9 @@ struct StepParams {
   int32_t flat;        // one tensor: block b starts at b*kBlock (no table load)
   int32_t any_sync;    // some tensor is averaged (else no tensor-table load)
   int64_t d;
+  // global sign given as bit planes (apply mode): [ld/64] each, zero may be null
+  const uint64_t* sign_bits;
+  const uint64_t* zero_bits;
   // optional outputs
   uint64_t* bits;
   int8_t* codes;
@@ -89,6 +92,9 @@ struct M1Params {
   int64_t d;
   float beta1, omega1;
 };
+
+// Aggregation modes of the fused step kernel.
+enum Agg : int { kAggVote = 0, kAggL1 = 1, kAggAvg = 2, kAggApply = 3 };
 
 // Block b's descriptor; a single-tensor vector needs no table load.
 __device__ __forceinline__ BlockEnt block_of(const BlockEnt* blk, int flat, int64_t d) {

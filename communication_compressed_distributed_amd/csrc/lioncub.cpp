@@ -25,6 +25,13 @@ hipError_t launch_pack(const float* x, uint64_t* bits, int64_t d, int64_t ld, in
                        uint32_t parity, hipStream_t st);
 hipError_t launch_vote(const uint64_t* bits, uint8_t* counts, int8_t* sign, int64_t d, int64_t ld,
                        int W, uint32_t parity, int tie_zero, hipStream_t st);
+hipError_t launch_vote_bits(const uint64_t* bits, uint64_t* sign_bits, uint64_t* zero_bits,
+                            int64_t d, int64_t ld, int W, uint32_t parity, int tie_zero,
+                            hipStream_t st);
+hipError_t launch_pack_codes(const int8_t* codes, uint32_t* wire, int64_t d, int64_t ld, int W,
+                             int n, hipStream_t st);
+hipError_t launch_unpack_sum(const uint32_t* wire, int32_t* sums, int8_t* sign, int64_t d,
+                             int64_t ld, int W, int n, hipStream_t st);
 }  // namespace lioncub
 
 using namespace lioncub;
@@ -73,7 +80,8 @@ int check_config(const lioncub_config* c, int64_t* nblk, int64_t* ngrp) {
   if ((c->theta_dtype != LIONCUB_F32 && c->theta_dtype != LIONCUB_BF16) ||
       (c->grad_dtype != LIONCUB_F32 && c->grad_dtype != LIONCUB_BF16))
     return LIONCUB_EINVAL;
-  if (c->agg != LIONCUB_AGG_VOTE && c->agg != LIONCUB_AGG_L1SUM) return LIONCUB_EINVAL;
+  if (c->agg != LIONCUB_AGG_VOTE && c->agg != LIONCUB_AGG_L1SUM && c->agg != LIONCUB_AGG_AVG)
+    return LIONCUB_EINVAL;
   if (c->agg == LIONCUB_AGG_L1SUM && (c->qbits < 2 || c->qbits > 8)) return LIONCUB_EINVAL;
   if (c->tie_mode != LIONCUB_TIE_PARITY && c->tie_mode != LIONCUB_TIE_ZERO) return LIONCUB_EINVAL;
   if (!finite(c->beta1) || !finite(c->beta2) || !finite(c->lr) || !finite(c->wd))
@@ -287,6 +295,8 @@ int lioncub_step(lioncub_ctx* ctx, void* theta, float* m, const void* g, int64_t
   p.g = g;
   p.parity = static_cast<int32_t>(t & 1);
   p.avg_step = (t % cf.sync_every) == 0;
+  const int kind = l1 ? LIONCUB_K_L1_STEP
+                     : (cf.agg == LIONCUB_AGG_AVG ? LIONCUB_K_AVG_STEP : LIONCUB_K_VOTE_STEP);
   if (dbg) {
     if ((dbg->bits || dbg->counts) && l1) return LIONCUB_EINVAL;
     if ((dbg->codes || dbg->sums || dbg->m1) && !l1) return LIONCUB_EINVAL;
@@ -311,12 +321,66 @@ int lioncub_step(lioncub_ctx* ctx, void* theta, float* m, const void* g, int64_t
       e = run(ctx, LIONCUB_K_M1_FINALIZE, [&] { return launch_m1_finalize(q, ctx->stream); });
   }
   if (e == hipSuccess)
-    e = run(ctx, l1 ? LIONCUB_K_L1_STEP : LIONCUB_K_VOTE_STEP, [&] {
-      return launch_step(p, ctx->nblk, cf.theta_dtype, cf.grad_dtype, l1 ? 1 : 0, ctx->stream);
+    e = run(ctx, kind, [&] {
+      return launch_step(p, ctx->nblk, cf.theta_dtype, cf.grad_dtype, cf.agg, ctx->stream);
     });
   if (e == hipSuccess && p.bits)
     e = launch_zero_tail_words(p.bits, cf.ld / 64, (cf.d + 63) / 64, cf.W, ctx->stream);
   return dev_status(e);
+}
+
+int lioncub_vote_bits(lioncub_ctx* ctx, const uint64_t* bits, int64_t t, uint64_t* sign_bits,
+                      uint64_t* zero_bits) {
+  if (!ctx || !bits || !sign_bits || t < 1) return LIONCUB_EINVAL;
+  if (!aligned(bits, 16) || !aligned(sign_bits, 16) || !aligned(zero_bits, 16))
+    return LIONCUB_EALIGN;
+  const lioncub_config& cf = ctx->cfg;
+  return dev_status(run(ctx, LIONCUB_K_VOTE_BITS, [&] {
+    return launch_vote_bits(bits, sign_bits, zero_bits, cf.d, cf.ld, cf.W,
+                            static_cast<uint32_t>(t & 1), cf.tie_mode == LIONCUB_TIE_ZERO,
+                            ctx->stream);
+  }));
+}
+
+int lioncub_apply(lioncub_ctx* ctx, void* theta, float* m, const void* g, int64_t t,
+                  const uint64_t* sign_bits, const uint64_t* zero_bits) {
+  if (!ctx || !theta || !m || !g || !sign_bits || t < 1) return LIONCUB_EINVAL;
+  if (!aligned(theta, 16) || !aligned(m, 16) || !aligned(g, 16) || !aligned(sign_bits, 16) ||
+      !aligned(zero_bits, 16))
+    return LIONCUB_EALIGN;
+  const lioncub_config& cf = ctx->cfg;
+  StepParams p;
+  fill_step_params(ctx, &p);
+  p.theta = theta;
+  p.m = m;
+  p.g = g;
+  p.parity = static_cast<int32_t>(t & 1);
+  p.avg_step = (t % cf.sync_every) == 0;
+  p.sign_bits = sign_bits;
+  p.zero_bits = zero_bits;
+  return dev_status(run(ctx, LIONCUB_K_APPLY, [&] {
+    return launch_step(p, ctx->nblk, cf.theta_dtype, cf.grad_dtype, kAggApply, ctx->stream);
+  }));
+}
+
+int lioncub_pack_codes(lioncub_ctx* ctx, const int8_t* codes, uint32_t* wire) {
+  if (!ctx || !codes || !wire) return LIONCUB_EINVAL;
+  if (ctx->cfg.qbits < 2 || ctx->cfg.qbits > 8) return LIONCUB_EINVAL;
+  if (!aligned(codes, 16) || !aligned(wire, 16)) return LIONCUB_EALIGN;
+  const lioncub_config& cf = ctx->cfg;
+  return dev_status(run(ctx, LIONCUB_K_PACK_CODES, [&] {
+    return launch_pack_codes(codes, wire, cf.d, cf.ld, cf.W, cf.qbits, ctx->stream);
+  }));
+}
+
+int lioncub_unpack_sum(lioncub_ctx* ctx, const uint32_t* wire, int32_t* sums, int8_t* sign) {
+  if (!ctx || !wire || (!sums && !sign)) return LIONCUB_EINVAL;
+  if (ctx->cfg.qbits < 2 || ctx->cfg.qbits > 8) return LIONCUB_EINVAL;
+  if (!aligned(wire, 16) || !aligned(sums, 16) || !aligned(sign, 16)) return LIONCUB_EALIGN;
+  const lioncub_config& cf = ctx->cfg;
+  return dev_status(run(ctx, LIONCUB_K_UNPACK_SUM, [&] {
+    return launch_unpack_sum(wire, sums, sign, cf.d, cf.ld, cf.W, cf.qbits, ctx->stream);
+  }));
 }
 
 int lioncub_pack(lioncub_ctx* ctx, const float* x, int64_t t, uint64_t* bits) {

@@ -74,7 +74,7 @@ __device__ __forceinline__ void step_block(const StepParams& p, const BlockEnt& 
   // for all of them before its first product; an LDS read is counted apart
   // from the memory loads and arrives first.
   __shared__ double sh_sc[256];
-  if (AGG == 1) {
+  if (AGG == kAggL1) {
     for (int i = tid; i < W; i += kThreads) sh_sc[i] = scl[static_cast<int64_t>(i) * p.nT];
     __syncthreads();
   }
@@ -83,7 +83,7 @@ __device__ __forceinline__ void step_block(const StepParams& p, const BlockEnt& 
 #pragma unroll 1
   for (int i0 = 0; i0 < W; i0 += WB) {
     double sc_b[WB];
-    if (AGG == 1) {
+    if (AGG == kAggL1) {
 #pragma unroll
       for (int b = 0; b < WB; ++b) sc_b[b] = (kExact || i0 + b < W) ? sh_sc[i0 + b] : 0.0;
     }
@@ -106,7 +106,7 @@ __device__ __forceinline__ void step_block(const StepParams& p, const BlockEnt& 
     for (int b = 0; b < WB; ++b) {
       const int i = i0 + b;
       if (!kExact && i >= W) break;
-      const double s_i = AGG == 1 ? sc_b[b] : 0.0;
+      const double s_i = AGG == kAggL1 ? sc_b[b] : 0.0;
 #pragma unroll
       for (int q = 0; q < Q; ++q) {
         const int64_t idx = static_cast<int64_t>(i) * p.ld + j[q];
@@ -115,9 +115,9 @@ __device__ __forceinline__ void step_block(const StepParams& p, const BlockEnt& 
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           const float c = (p.beta1 * mv[b][q].v[k]) + (p.omega1 * gv[b][q].v[k]);
-          if (AGG == 0) {
+          if (AGG == kAggVote || AGG == kAggAvg) {
             nib |= ((FULL || k < nv[q]) ? sign_bit(c, par) : 0u) << k;
-          } else {
+          } else if (AGG == kAggL1) {
             double y = __builtin_rint(static_cast<double>(c) * s_i);
             y = fmin(fmax(y, -static_cast<double>(p.qmax)), static_cast<double>(p.qmax));
             const int qc = static_cast<int>(y);
@@ -126,14 +126,14 @@ __device__ __forceinline__ void step_block(const StepParams& p, const BlockEnt& 
           }
           mn.v[k] = (p.beta2 * mv[b][q].v[k]) + (p.omega2 * gv[b][q].v[k]);
         }
-        if (AGG == 0) {
+        if (AGG == kAggVote || AGG == kAggAvg) {
           cnt[q] += nibble_to_bytes(nib);
           if (DBG && p.bits) {
             const uint64_t word = wave_pack_words(nib);  // every lane takes part
             if ((tid & 15) == 0 && (FULL || nv[q] > 0))
               p.bits[static_cast<int64_t>(i) * (p.ld >> 6) + (j[q] >> 6)] = word;
           }
-        } else if (DBG && p.codes && (FULL || nv[q] > 0)) {
+        } else if (AGG == kAggL1 && DBG && p.codes && (FULL || nv[q] > 0)) {
           st_b4(p.codes + idx, nib, nv[q]);
         }
         if (FULL || nv[q] > 0) {
@@ -153,19 +153,44 @@ __device__ __forceinline__ void step_block(const StepParams& p, const BlockEnt& 
 #pragma unroll
   for (int q = 0; q < Q; ++q) {
     if (!FULL && nv[q] == 0) continue;
-    // global sign
+    // global sign s (the int8 record) and the applied update sf
     int s[4];
-    if (AGG == 0) {
+    float sf[4];
+    if (AGG == kAggVote) {
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const int twice = 2 * static_cast<int>((cnt[q] >> (8 * k)) & 0xFFu);
         s[k] = twice > W ? 1 : (twice < W ? -1 : (p.tie_zero ? 0 : (par ? 1 : -1)));
+        sf[k] = static_cast<float>(s[k]);
       }
       if (DBG && p.counts) st_b4(p.counts + j[q], cnt[q], nv[q]);
-    } else {
+    } else if (AGG == kAggAvg) {
+      // D-Lion averaging: the mean of the W signs, (2v - W) / W in fp32
 #pragma unroll
-      for (int k = 0; k < 4; ++k) s[k] = (sum[q][k] > 0) - (sum[q][k] < 0);
+      for (int k = 0; k < 4; ++k) {
+        const int net = 2 * static_cast<int>((cnt[q] >> (8 * k)) & 0xFFu) - W;
+        s[k] = (net > 0) - (net < 0);
+        sf[k] = static_cast<float>(net) / static_cast<float>(W);
+      }
+      if (DBG && p.counts) st_b4(p.counts + j[q], cnt[q], nv[q]);
+    } else if (AGG == kAggL1) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        s[k] = (sum[q][k] > 0) - (sum[q][k] < 0);
+        sf[k] = static_cast<float>(s[k]);
+      }
       if (DBG && p.sums) st_i32x4(p.sums + j[q], sum[q], nv[q]);
+    } else {
+      // apply mode: the sign arrives as bit planes (16 lanes share a word)
+      const int sh = static_cast<int>(j[q] & 63);
+      const uint32_t pos = static_cast<uint32_t>(p.sign_bits[j[q] >> 6] >> sh) & 0xFu;
+      const uint32_t zer =
+          p.zero_bits ? static_cast<uint32_t>(p.zero_bits[j[q] >> 6] >> sh) & 0xFu : 0u;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        s[k] = ((zer >> k) & 1u) ? 0 : (((pos >> k) & 1u) ? 1 : -1);
+        sf[k] = static_cast<float>(s[k]);
+      }
     }
     if (DBG && p.sign) {
       const uint32_t packed = (static_cast<uint32_t>(s[0]) & 0xFFu) |
@@ -178,7 +203,7 @@ __device__ __forceinline__ void step_block(const StepParams& p, const BlockEnt& 
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const float x = th[q].v[k];
-      th[q].v[k] = x - (p.lr * (static_cast<float>(s[k]) + (p.wd * x)));
+      th[q].v[k] = x - (p.lr * (sf[k] + (p.wd * x)));
     }
     st_x4<TT>(p.theta, j[q], th[q], nv[q]);
     // worker mean of the new momenta on averaging steps
@@ -242,14 +267,15 @@ static hipError_t launch_t(const StepParams& p, int nblk, hipStream_t st) {
 hipError_t launch_step(const StepParams& p, int nblk, int theta_bf16, int grad_bf16, int agg,
                        hipStream_t st) {
   const bool dbg = p.bits || p.codes || p.counts || p.sums || p.sign;
-  const int key = (theta_bf16 << 3) | (grad_bf16 << 2) | ((dbg ? 1 : 0) << 1) | agg;
+  const int key = (theta_bf16 << 4) | (grad_bf16 << 3) | ((dbg ? 1 : 0) << 2) | agg;
   switch (key) {
 #define LC_CASE(TT, GT, D, A) \
-  case ((TT << 3) | (GT << 2) | (D << 1) | A): return launch_t<TT, GT, (D != 0), A>(p, nblk, st);
-    LC_CASE(0, 0, 0, 0) LC_CASE(0, 0, 0, 1) LC_CASE(0, 0, 1, 0) LC_CASE(0, 0, 1, 1)
-    LC_CASE(0, 1, 0, 0) LC_CASE(0, 1, 0, 1) LC_CASE(0, 1, 1, 0) LC_CASE(0, 1, 1, 1)
-    LC_CASE(1, 0, 0, 0) LC_CASE(1, 0, 0, 1) LC_CASE(1, 0, 1, 0) LC_CASE(1, 0, 1, 1)
-    LC_CASE(1, 1, 0, 0) LC_CASE(1, 1, 0, 1) LC_CASE(1, 1, 1, 0) LC_CASE(1, 1, 1, 1)
+  case ((TT << 4) | (GT << 3) | (D << 2) | A): return launch_t<TT, GT, (D != 0), A>(p, nblk, st);
+#define LC_AGGS(TT, GT, D) LC_CASE(TT, GT, D, 0) LC_CASE(TT, GT, D, 1) LC_CASE(TT, GT, D, 2)
+    LC_AGGS(0, 0, 0) LC_AGGS(0, 0, 1) LC_AGGS(0, 1, 0) LC_AGGS(0, 1, 1)
+    LC_AGGS(1, 0, 0) LC_AGGS(1, 0, 1) LC_AGGS(1, 1, 0) LC_AGGS(1, 1, 1)
+    LC_CASE(0, 0, 0, 3) LC_CASE(0, 1, 0, 3) LC_CASE(1, 0, 0, 3) LC_CASE(1, 1, 0, 3)
+#undef LC_AGGS
 #undef LC_CASE
     default: return hipErrorInvalidValue;
   }

@@ -1,0 +1,215 @@
+// wire.hip -- receive-side and wire-format kernels of the worker-sharded
+// exchange, gfx950.
+//
+// On a cluster the pages' 1-bit path sends packed sign bitmaps through an
+// AlltoAll, each worker votes on its slice and the 1-bit result is
+// all-gathered; the p-bit path sends n-bit Eq. (1) codes and sums them
+// ("Lion Cub: Minimizing Communication Overhead in Distributed Lion",
+// pith.science review: "What carries the argument", the Figure 1 caption,
+// the referee report on summation width).  These kernels are the per-GPU
+// halves of that exchange, so the single-GPU pieces compose into it:
+//
+//   vote_bits:  W bitmaps -> the global sign as bit planes (sign, zero)
+//   pack_codes: int8 codes -> n-bit two's complement fields, 32 elements per
+//               group of n 32-bit words
+//   unpack_sum: W packed rows -> int32 sums and their signs
+//
+// (Applying a global sign bitmap to theta and the momenta is a mode of the
+// fused step kernel.)
+#include "device.hpp"
+#include "layout.hpp"
+
+namespace lioncub {
+
+struct VoteBitsParams {
+  const uint64_t* bits;  // [W][words]
+  uint64_t* sign_bits;   // [words]
+  uint64_t* zero_bits;   // [words] or null
+  int64_t d, words;
+  int32_t W;
+  uint32_t parity;
+  int32_t tie_zero;
+};
+
+// grid: ceil(ld/1024); 256 threads, a quad of elements per thread; counts in
+// four byte lanes of one register, planes assembled by wave ballots.
+__global__ __launch_bounds__(kThreads) void k_vote_bits(VoteBitsParams p) {
+  const int tid = threadIdx.x;
+  const int64_t j = (static_cast<int64_t>(blockIdx.x) * kThreads + tid) * kQuad;
+  const int64_t rem = p.d - j;
+  const int nv = rem >= 4 ? 4 : (rem > 0 ? static_cast<int>(rem) : 0);
+  uint32_t pos = 0, zer = 0;
+  if (nv > 0) {
+    const uint64_t* __restrict__ col = p.bits + (j >> 6);
+    const int sh = static_cast<int>(j & 63);
+    uint32_t cnt = 0;
+    int i = 0;
+    for (; i + 8 <= p.W; i += 8) {
+      uint64_t w[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) w[u] = col[static_cast<int64_t>(i + u) * p.words];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) cnt += nibble_to_bytes(static_cast<uint32_t>(w[u] >> sh) & 0xFu);
+    }
+    for (; i < p.W; ++i)
+      cnt += nibble_to_bytes(static_cast<uint32_t>(col[static_cast<int64_t>(i) * p.words] >> sh) & 0xFu);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      if (k >= nv) break;
+      const int twice = 2 * static_cast<int>((cnt >> (8 * k)) & 0xFFu);
+      const int s = twice > p.W ? 1 : (twice < p.W ? -1 : (p.tie_zero ? 0 : (p.parity ? 1 : -1)));
+      pos |= (s > 0 ? 1u : 0u) << k;
+      zer |= (s == 0 ? 1u : 0u) << k;
+    }
+  }
+  const uint64_t wpos = wave_pack_words(pos);
+  const uint64_t wzer = wave_pack_words(zer);
+  if ((tid & 15) == 0 && (j >> 6) < p.words) {
+    p.sign_bits[j >> 6] = wpos;
+    if (p.zero_bits) p.zero_bits[j >> 6] = wzer;
+  }
+}
+
+struct WireParams {
+  const int8_t* codes;   // [W][ld]
+  uint32_t* wire;        // [W][(ld/32)*n]
+  int32_t* sums;         // [d] or null
+  int8_t* sign;          // [d] or null
+  int64_t d, ld;
+  int32_t W;
+};
+
+// One thread per (worker, group of 32 elements): 32 codes (two 16-byte
+// loads) -> N words.  Field k sits at bit N*k of the group's bit string; all
+// positions are compile-time, so a field that straddles two words is two
+// shifts.
+template <int N>
+__global__ __launch_bounds__(kThreads) void k_pack_codes(WireParams p) {
+  const int64_t groups = p.ld >> 5;
+  const int64_t gid = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  if (gid >= groups * p.W) return;
+  const int64_t i = gid / groups, gi = gid % groups;
+  const int64_t j0 = gi << 5;
+  const int8_t* src = p.codes + i * p.ld + j0;
+  uint32_t c[8];
+  const uint4 a = *reinterpret_cast<const uint4*>(src);
+  const uint4 b = *reinterpret_cast<const uint4*>(src + 16);
+  c[0] = a.x; c[1] = a.y; c[2] = a.z; c[3] = a.w;
+  c[4] = b.x; c[5] = b.y; c[6] = b.z; c[7] = b.w;
+  const int64_t valid = p.d - j0;  // elements at or past d pack as 0
+  uint32_t w[N];
+#pragma unroll
+  for (int k = 0; k < N; ++k) w[k] = 0;
+  constexpr uint32_t mask = (1u << N) - 1u;
+#pragma unroll
+  for (int k = 0; k < 32; ++k) {
+    const uint32_t f = k < valid ? ((c[k >> 2] >> (8 * (k & 3))) & mask) : 0u;
+    const int bit = N * k;
+    w[bit >> 5] |= f << (bit & 31);
+    if ((bit & 31) + N > 32) w[(bit >> 5) + 1] |= f >> (32 - (bit & 31));
+  }
+  uint32_t* dst = p.wire + i * (groups * N) + gi * N;
+#pragma unroll
+  for (int k = 0; k < N; ++k) dst[k] = w[k];
+}
+
+// One thread per group of 32 elements: for every worker, N words -> 32
+// sign-extended fields added to 32 int32 sums; then sums and signs stored.
+template <int N>
+__global__ __launch_bounds__(kThreads) void k_unpack_sum(WireParams p) {
+  const int64_t groups = p.ld >> 5;
+  const int64_t gi = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  const int64_t j0 = gi << 5;
+  if (j0 >= p.d) return;
+  int32_t S[32];
+#pragma unroll
+  for (int k = 0; k < 32; ++k) S[k] = 0;
+#pragma unroll 1
+  for (int i = 0; i < p.W; ++i) {
+    const uint32_t* src = p.wire + static_cast<int64_t>(i) * (groups * N) + gi * N;
+    uint32_t w[N];
+#pragma unroll
+    for (int k = 0; k < N; ++k) w[k] = src[k];
+#pragma unroll
+    for (int k = 0; k < 32; ++k) {
+      const int bit = N * k;
+      uint32_t f = w[bit >> 5] >> (bit & 31);
+      if ((bit & 31) + N > 32) f |= w[(bit >> 5) + 1] << (32 - (bit & 31));
+      // sign-extend the low N bits
+      const int32_t q = static_cast<int32_t>(f << (32 - N)) >> (32 - N);
+      S[k] += q;
+    }
+  }
+  const int64_t valid = p.d - j0;
+  if (valid >= 32) {
+    if (p.sums) {
+#pragma unroll
+      for (int k = 0; k < 32; k += 4)
+        *reinterpret_cast<int4*>(p.sums + j0 + k) = make_int4(S[k], S[k + 1], S[k + 2], S[k + 3]);
+    }
+    if (p.sign) {
+      uint32_t sg[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) sg[k] = 0;
+#pragma unroll
+      for (int k = 0; k < 32; ++k)
+        sg[k >> 2] |= (static_cast<uint32_t>((S[k] > 0) - (S[k] < 0)) & 0xFFu) << (8 * (k & 3));
+      *reinterpret_cast<uint4*>(p.sign + j0) = make_uint4(sg[0], sg[1], sg[2], sg[3]);
+      *reinterpret_cast<uint4*>(p.sign + j0 + 16) = make_uint4(sg[4], sg[5], sg[6], sg[7]);
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < 32; ++k) {
+      if (k >= valid) break;
+      if (p.sums) p.sums[j0 + k] = S[k];
+      if (p.sign) p.sign[j0 + k] = static_cast<int8_t>((S[k] > 0) - (S[k] < 0));
+    }
+  }
+}
+
+hipError_t launch_vote_bits(const uint64_t* bits, uint64_t* sign_bits, uint64_t* zero_bits,
+                            int64_t d, int64_t ld, int W, uint32_t parity, int tie_zero,
+                            hipStream_t st) {
+  VoteBitsParams p{bits, sign_bits, zero_bits, d, ld >> 6, W, parity, tie_zero};
+  const int64_t grid = (ld + kThreads * kQuad - 1) / (kThreads * kQuad);
+  hipLaunchKernelGGL(k_vote_bits, dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, st, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_codes(const int8_t* codes, uint32_t* wire, int64_t d, int64_t ld, int W,
+                             int n, hipStream_t st) {
+  WireParams p{codes, wire, nullptr, nullptr, d, ld, W};
+  const int64_t threads = (ld >> 5) * W;
+  const dim3 g(static_cast<unsigned>((threads + kThreads - 1) / kThreads)), b(kThreads);
+  switch (n) {
+    case 2: hipLaunchKernelGGL(k_pack_codes<2>, g, b, 0, st, p); break;
+    case 3: hipLaunchKernelGGL(k_pack_codes<3>, g, b, 0, st, p); break;
+    case 4: hipLaunchKernelGGL(k_pack_codes<4>, g, b, 0, st, p); break;
+    case 5: hipLaunchKernelGGL(k_pack_codes<5>, g, b, 0, st, p); break;
+    case 6: hipLaunchKernelGGL(k_pack_codes<6>, g, b, 0, st, p); break;
+    case 7: hipLaunchKernelGGL(k_pack_codes<7>, g, b, 0, st, p); break;
+    case 8: hipLaunchKernelGGL(k_pack_codes<8>, g, b, 0, st, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_unpack_sum(const uint32_t* wire, int32_t* sums, int8_t* sign, int64_t d,
+                             int64_t ld, int W, int n, hipStream_t st) {
+  WireParams p{nullptr, const_cast<uint32_t*>(wire), sums, sign, d, ld, W};
+  const int64_t threads = (d + 31) >> 5;
+  const dim3 g(static_cast<unsigned>((threads + kThreads - 1) / kThreads)), b(kThreads);
+  switch (n) {
+    case 2: hipLaunchKernelGGL(k_unpack_sum<2>, g, b, 0, st, p); break;
+    case 3: hipLaunchKernelGGL(k_unpack_sum<3>, g, b, 0, st, p); break;
+    case 4: hipLaunchKernelGGL(k_unpack_sum<4>, g, b, 0, st, p); break;
+    case 5: hipLaunchKernelGGL(k_unpack_sum<5>, g, b, 0, st, p); break;
+    case 6: hipLaunchKernelGGL(k_unpack_sum<6>, g, b, 0, st, p); break;
+    case 7: hipLaunchKernelGGL(k_unpack_sum<7>, g, b, 0, st, p); break;
+    case 8: hipLaunchKernelGGL(k_unpack_sum<8>, g, b, 0, st, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace lioncub

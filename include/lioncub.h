@@ -66,7 +66,7 @@ enum {
 };
 
 enum { LIONCUB_F32 = 0, LIONCUB_BF16 = 1 };
-enum { LIONCUB_AGG_VOTE = 0, LIONCUB_AGG_L1SUM = 1 };
+enum { LIONCUB_AGG_VOTE = 0, LIONCUB_AGG_L1SUM = 1, LIONCUB_AGG_AVG = 2 };
 enum { LIONCUB_TIE_PARITY = 0, LIONCUB_TIE_ZERO = 1 };
 
 typedef struct {
@@ -83,7 +83,11 @@ typedef struct {
   int32_t sync_every;            /* >= 1: averaging on steps with t % sync_every == 0 */
   int32_t theta_dtype;           /* LIONCUB_F32 or LIONCUB_BF16                  */
   int32_t grad_dtype;            /* LIONCUB_F32 or LIONCUB_BF16; m is always fp32 */
-  int32_t agg;                   /* LIONCUB_AGG_VOTE or LIONCUB_AGG_L1SUM        */
+  int32_t agg;                   /* LIONCUB_AGG_VOTE (majority vote of the sign
+                                    bitmaps), LIONCUB_AGG_L1SUM (integer sum of
+                                    Eq. (1) codes) or LIONCUB_AGG_AVG (D-Lion
+                                    averaging: the applied update is the mean
+                                    of the W signs, (2*count - W) / W in fp32) */
   int32_t qbits;                 /* n of Eq. (1), 2..8; required for L1SUM and for
                                     lioncub_quant_l1, else ignored               */
   int32_t tie_mode;              /* vote ties (2*count == W): LIONCUB_TIE_PARITY
@@ -152,6 +156,45 @@ int lioncub_vote(lioncub_ctx *ctx, const uint64_t *bits, int64_t t, uint8_t *cou
  * with mean 0 gets all-zero codes.  Needs qbits in 2..8 in the config. */
 int lioncub_quant_l1(lioncub_ctx *ctx, const float *x, int8_t *codes, double *m1);
 
+/* ---- receive side and wire formats of the worker-sharded exchange -------
+ * Sources: "Lion Cub: Minimizing Communication Overhead in Distributed Lion",
+ * pith.science review ("What carries the argument": the 1-bit path packs
+ * signs, votes and all-gathers a 1-bit result; the p-bit path sums n-bit
+ * codes; Figure 1 caption; the referee report's note that the sum needs more
+ * bits than a code).  On one GPU these operate on the context's whole
+ * vector; on a cluster each GPU would run them on its slice.              */
+
+/* Global sign of the majority vote over bits[W][ld/64] (device) as bit
+ * planes: sign_bits[ld/64] (device, required) gets bit 1 where the sign is
+ * +1; zero_bits[ld/64] (device, may be NULL) gets bit 1 where it is 0 (ties
+ * under LIONCUB_TIE_ZERO; under LIONCUB_TIE_PARITY a tie is carried by the
+ * parity of t in the sign plane, as a 1-bit all-gather carries it).  Every
+ * word is written; bits past d are 0. */
+int lioncub_vote_bits(lioncub_ctx *ctx, const uint64_t *bits, int64_t t,
+                      uint64_t *sign_bits, uint64_t *zero_bits);
+
+/* Steps 4-5 from a global sign given as bit planes (as lioncub_vote_bits
+ * writes them; zero_bits may be NULL = no zeros): theta <- theta - lr*(s +
+ * wd*theta) with s = zero ? 0 : (sign ? +1 : -1), then every worker's
+ * momentum update and the selective averaging, exactly as lioncub_step.
+ * theta/m/g as in lioncub_step; sign_bits/zero_bits device [ld/64]. */
+int lioncub_apply(lioncub_ctx *ctx, void *theta, float *m, const void *g, int64_t t,
+                  const uint64_t *sign_bits, const uint64_t *zero_bits);
+
+/* n-bit wire packing of Eq. (1) codes, n = qbits of the config (2..8):
+ * codes[W][ld] (device int8; values in [-(2^(n-1)-1), 2^(n-1)-1]; columns
+ * j >= d ignored) -> wire[W][(ld/32)*n] (device uint32).  Per row, each 32
+ * elements form a group of n words; element k of a group is the n-bit two's
+ * complement field at bit n*k of the group's little-endian bit string.
+ * Elements past d pack as 0. */
+int lioncub_pack_codes(lioncub_ctx *ctx, const int8_t *codes, uint32_t *wire);
+
+/* Receive side of the p-bit exchange: for every element, the W workers'
+ * fields are unpacked from wire[W][(ld/32)*n] (device) and summed in int32:
+ * sums[d] (device, may be NULL) and sign[d] (device int8, may be NULL; sgn,
+ * 0 for a zero sum).  At least one output must be given. */
+int lioncub_unpack_sum(lioncub_ctx *ctx, const uint32_t *wire, int32_t *sums, int8_t *sign);
+
 /* Measurement hook: while enabled, every kernel the context launches is
  * bracketed by HIP events on its stream (at most `capacity` launches are
  * recorded).  lioncub_profile_end synchronises on the events, disables the
@@ -166,7 +209,12 @@ enum {
   LIONCUB_K_PACK = 4,
   LIONCUB_K_VOTE = 5,
   LIONCUB_K_QUANT = 6,
-  LIONCUB_K_COUNT = 7
+  LIONCUB_K_VOTE_BITS = 7,
+  LIONCUB_K_APPLY = 8,
+  LIONCUB_K_PACK_CODES = 9,
+  LIONCUB_K_UNPACK_SUM = 10,
+  LIONCUB_K_AVG_STEP = 11,
+  LIONCUB_K_COUNT = 12
 };
 int lioncub_profile_begin(lioncub_ctx *ctx, int32_t capacity);
 int lioncub_profile_end(lioncub_ctx *ctx, double *ms_total, int32_t *launches);

@@ -99,7 +99,7 @@ def gpu_step_vs_oracle(wl, steps=2, t0=1, zeros=True, debug=True, seed_shift=0):
         dbg = None
         if debug:
             dbg = {"sign": torch.zeros(wl.d, dtype=torch.int8, device="cuda")}
-            if wl.agg == "vote":
+            if wl.agg in ("vote", "avg"):
                 dbg["bits"] = torch.full((wl.W, wl.ld // 64), -1, dtype=torch.int64, device="cuda")
                 dbg["counts"] = torch.zeros(wl.d, dtype=torch.uint8, device="cuda")
             else:
@@ -112,7 +112,7 @@ def gpu_step_vs_oracle(wl, steps=2, t0=1, zeros=True, debug=True, seed_shift=0):
         check_float_state(f"m t={t}", to_host(d_m)[:, : wl.d], m[:, : wl.d])
         if debug:
             got_sign = to_host(dbg["sign"])
-            if wl.agg == "vote":
+            if wl.agg in ("vote", "avg"):
                 gb_ = to_host(dbg["bits"]).view(np.uint64)
                 assert np.array_equal(gb_, want["bits"]), f"bits t={t}"
                 gc = to_host(dbg["counts"])

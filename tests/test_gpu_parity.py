@@ -255,3 +255,168 @@ def test_bad_arguments_on_device():
     with pytest.raises(LionCubError):
         lc.quant_l1(m, torch.zeros((4, 4096), dtype=torch.int8, device="cuda"))  # no qbits
     lc.close()
+
+
+# -------------------- D-Lion averaging, receive side and wire formats ----
+
+AVG = {
+    "avg-W4": wls.flat("a1", 3 * 4096 + 300, W=4, agg="avg"),
+    "avg-W3-bf16": wls.flat("a2", 2 * 4096 + 4099, W=3, agg="avg", theta_dtype="bf16",
+                            grad_dtype="bf16"),
+    "avg-W16-sync": wls.Workload(name="a3", tensors=[("wte", 4096 + 64), ("h", 8192)], W=16,
+                                 agg="avg", sync_names=("wte",), sync_every=2),
+    "avg-W8-gpt": small(wls.GPT2_124M_W8_VOTE.with_(agg="avg"), 4096 + 640, 20),
+}
+
+
+@pytest.mark.parametrize("debug", [True, False], ids=["debug", "production"])
+@pytest.mark.parametrize("name", list(AVG))
+def test_avg_parity(name, debug):
+    res = gpu_step_vs_oracle(AVG[name], steps=3, debug=debug)
+    print(name, res, flush=True)
+
+
+@pytest.mark.parametrize("W", [1, 3, 4, 8, 16, 255])
+@pytest.mark.parametrize("tie", ["parity", "zero"])
+def test_vote_bits_parity(W, tie):
+    import torch
+    rs = np.random.default_rng(W)
+    d = 2 * 4096 + 777
+    ld = (d + 63) // 64 * 64 + 64
+    wl, lc = _ctx(W, d, ld=ld, tie=tie)
+    tm = lco.TIE_ZERO if tie == "zero" else lco.TIE_PARITY
+    for t in (1, 2):
+        x = rs.standard_normal((W, ld)).astype(np.float32)
+        x[rs.random((W, ld)) < 0.05] = 0.0
+        bits = lco.pack(x, d, t)
+        sb = torch.full((ld // 64,), -1, dtype=torch.int64, device="cuda")
+        zb = torch.full((ld // 64,), -1, dtype=torch.int64, device="cuda")
+        lc.vote_bits(to_dev(bits.view(np.int64)), t, sb, zb)
+        sb1 = torch.full((ld // 64,), -1, dtype=torch.int64, device="cuda")
+        lc.vote_bits(to_dev(bits.view(np.int64)), t, sb1)
+        torch.cuda.synchronize()
+        wsb, wzb = lco.vote_bits(bits, W, d, t, tm)
+        assert np.array_equal(to_host(sb).view(np.uint64), wsb)
+        assert np.array_equal(to_host(zb).view(np.uint64), wzb)
+        assert np.array_equal(to_host(sb1).view(np.uint64), wsb)
+    lc.close()
+
+
+APPLY = {
+    "apply-W4": wls.flat("p1", 3 * 4096 + 300, W=4),
+    "apply-W16-l1cfg": wls.flat("p2", 2 * 4096 + 4099, W=16, agg="l1", qbits=4),
+    "apply-W5-bf16-sync": wls.Workload(name="p3", tensors=[("wte", 4096 + 64), ("h", 4160)], W=5,
+                                       theta_dtype="bf16", grad_dtype="bf16",
+                                       sync_names=("wte",), sync_every=1),
+    "apply-W8-gpt": small(wls.GPT_760M_W8_VOTE_SYNC, 4096 + 640, 20),
+}
+
+
+@pytest.mark.parametrize("zero", [True, False])
+@pytest.mark.parametrize("name", list(APPLY))
+def test_apply_parity(name, zero):
+    import torch
+    from synth import gen
+    wl = APPLY[name]
+    rs = np.random.default_rng(3)
+    tb, gb = wl.theta_dtype == "bf16", wl.grad_dtype == "bf16"
+    theta, m = gen.host_theta(wl), gen.host_m(wl)
+    lc = lioncub_for(wl)
+    d_theta, d_m = to_dev(theta, tb), to_dev(m)
+    for t in (1, 2, 3):
+        g = gen.host_g(wl, t)
+        s = rs.integers(-1 if zero else 0, 2, wl.ld)
+        if not zero:
+            s = np.where(s == 0, -1, 1)
+        s[wl.d:] = 0
+        sb = np.packbits(s > 0, bitorder="little").view("<u8").copy()
+        zb = np.packbits(s == 0, bitorder="little").view("<u8").copy() if zero else None
+        lc.apply(d_theta, d_m, to_dev(g, gb), t, to_dev(sb.view(np.int64)),
+                 None if zb is None else to_dev(zb.view(np.int64)))
+        torch.cuda.synchronize()
+        lco.apply(wl, theta, m, g, t, sb, zb)
+        from tests.harness import check_float_state
+        check_float_state(f"theta t={t}", to_host(d_theta), theta, bf16=tb)
+        check_float_state(f"m t={t}", to_host(d_m)[:, :wl.d], m[:, :wl.d])
+    lc.close()
+
+
+@pytest.mark.parametrize("W", [4, 8, 16])
+def test_one_bit_path_composes_into_the_step(W):
+    """The worker-sharded 1-bit flow on one GPU: pack(c) -> vote_bits ->
+    apply gives exactly what the fused step gives (theta and m bit for bit)."""
+    import torch
+    from synth import gen
+    wl = wls.flat("c1b", 3 * 4096 + 128, W=W)
+    theta, m = gen.host_theta(wl), gen.host_m(wl)
+    g = gen.host_g(wl, 1)
+    c = np.zeros((W, wl.ld), np.float32)
+    for i in range(W):
+        c[i, : wl.d] = lco.c_row(wl, m[i, : wl.d], g[i, : wl.d])
+    lc = lioncub_for(wl)
+    thA, mA, dg = to_dev(theta), to_dev(m), to_dev(g)
+    lc.step(thA, mA, dg, 1)
+    thB, mB = to_dev(theta), to_dev(m)
+    bits = torch.empty((W, wl.ld // 64), dtype=torch.int64, device="cuda")
+    sb = torch.empty((wl.ld // 64,), dtype=torch.int64, device="cuda")
+    lc.pack(to_dev(c), 1, bits)
+    lc.vote_bits(bits, 1, sb)
+    lc.apply(thB, mB, dg, 1, sb)
+    torch.cuda.synchronize()
+    assert torch.equal(thA, thB) and torch.equal(mA, mB)
+    lc.close()
+
+
+@pytest.mark.parametrize("n", [2, 3, 4, 5, 6, 7, 8])
+@pytest.mark.parametrize("W", [1, 3, 16])
+def test_wire_pack_and_unpack_sum(n, W):
+    import torch
+    qmax = 2 ** (n - 1) - 1
+    rs = np.random.default_rng(10 * n + W)
+    d = 4096 + 1000 + 7
+    ld = (d + 63) // 64 * 64
+    wl, lc = _ctx(W, d, agg="l1", qbits=n)
+    codes = rs.integers(-qmax, qmax + 1, (W, ld)).astype(np.int8)   # junk past d too
+    wire = torch.full((W, (ld // 32) * n), -1, dtype=torch.int32, device="cuda")
+    lc.pack_codes(to_dev(codes), wire)
+    sums = torch.zeros(d, dtype=torch.int32, device="cuda")
+    sign = torch.zeros(d, dtype=torch.int8, device="cuda")
+    lc.unpack_sum(wire, sums, sign)
+    only_sign = torch.zeros(d, dtype=torch.int8, device="cuda")
+    lc.unpack_sum(wire, None, only_sign)
+    torch.cuda.synchronize()
+    ww = lco.pack_codes(codes, d, n)
+    assert np.array_equal(to_host(wire).view(np.uint32), ww)
+    ws, wsg = lco.unpack_sum(ww, W, d, ld, n)
+    assert np.array_equal(to_host(sums), ws)
+    assert np.array_equal(to_host(sign), wsg)
+    assert np.array_equal(to_host(only_sign), wsg)
+    lc.close()
+
+
+def test_p_bit_path_composes_into_the_step():
+    """quant_l1(c) -> pack_codes -> unpack_sum reproduces the fused L1 step's
+    integer sums and signs (debug outputs) bit for bit."""
+    import torch
+    from synth import gen
+    wl = wls.Workload(name="pb", tensors=[("a", 2 * 4096 + 192), ("b", 4096)], W=8, agg="l1",
+                      qbits=4)
+    theta, m = gen.host_theta(wl), gen.host_m(wl)
+    g = gen.host_g(wl, 1)
+    c = np.zeros((wl.W, wl.ld), np.float32)
+    for i in range(wl.W):
+        c[i, : wl.d] = lco.c_row(wl, m[i, : wl.d], g[i, : wl.d])
+    lc = lioncub_for(wl)
+    dbg = {"sums": torch.zeros(wl.d, dtype=torch.int32, device="cuda"),
+           "sign": torch.zeros(wl.d, dtype=torch.int8, device="cuda")}
+    lc.step(to_dev(theta), to_dev(m), to_dev(g), 1, dbg)
+    codes = torch.zeros((wl.W, wl.ld), dtype=torch.int8, device="cuda")
+    lc.quant_l1(to_dev(c), codes)
+    wire = torch.empty((wl.W, (wl.ld // 32) * wl.qbits), dtype=torch.int32, device="cuda")
+    lc.pack_codes(codes, wire)
+    sums = torch.zeros(wl.d, dtype=torch.int32, device="cuda")
+    sign = torch.zeros(wl.d, dtype=torch.int8, device="cuda")
+    lc.unpack_sum(wire, sums, sign)
+    torch.cuda.synchronize()
+    assert torch.equal(sums, dbg["sums"]) and torch.equal(sign, dbg["sign"])
+    lc.close()
