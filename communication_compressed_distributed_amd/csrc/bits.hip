@@ -11,10 +11,9 @@
 // elements 64k..64k+63 is assembled from bits 16k..16k+15 of the ballots by a
 // 4-way bit spread and stored by lane 16k.
 //
-// Vote: each lane owns a quad; for every worker it loads the 64-bit word that
-// holds its quad (16 lanes share one word: one cache line per 16 lanes),
-// extracts its nibble and adds it to four byte-wide counters held in one
-// register (W <= 255, so no byte overflows).
+// Vote: each lane owns one 64-element word column and counts with bit-sliced
+// adders; see k_vote_sliced.  Besides counts and signs it can emit the
+// global sign as bit planes (the receive side of the 1-bit exchange).
 #include "device.hpp"
 #include "layout.hpp"
 
@@ -27,80 +26,186 @@ struct PackParams {
   uint32_t parity;
 };
 
-// grid: (ceil(ld/1024), W); 256 threads; 1024 elements (16 words) per group.
+// grid: (ceil(ld/4096), W); 256 threads; 4096 elements (64 words) per
+// workgroup, 4 quads per thread (streaming 16-byte loads issued together).
 __global__ __launch_bounds__(kThreads) void k_pack(PackParams p) {
   const int tid = threadIdx.x;
   const int64_t i = blockIdx.y;
-  const int64_t j = static_cast<int64_t>(blockIdx.x) * (kThreads * kQuad) + kQuad * tid;
-  const int64_t rem = p.d - j;
-  const int nv = rem >= 4 ? 4 : (rem > 0 ? static_cast<int>(rem) : 0);
-  uint32_t nib = 0;
-  if (nv > 0) {
-    const F4 x = ld_f32x4(p.x + i * p.ld + j, nv);
+  const int64_t base = static_cast<int64_t>(blockIdx.x) * kBlock;
+  F4 x[kRounds];
+  int nv[kRounds];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) nib |= (k < nv ? sign_bit(x.v[k], p.parity) : 0u) << k;
+  for (int q = 0; q < kRounds; ++q) {
+    const int64_t j = base + kThreads * kQuad * q + kQuad * tid;
+    const int64_t rem = p.d - j;
+    nv[q] = rem >= 4 ? 4 : (rem > 0 ? static_cast<int>(rem) : 0);
+    if (nv[q] == 4) x[q] = ldnt_f32x4(p.x + i * p.ld + j, 4);
+    else if (nv[q] > 0) x[q] = ldm_f32x4(p.x + i * p.ld + j, nv[q]);
   }
-  const uint64_t word = wave_pack_words(nib);
-  if ((tid & 15) == 0 && j < p.ld) p.bits[i * (p.ld >> 6) + (j >> 6)] = word;
+#pragma unroll
+  for (int q = 0; q < kRounds; ++q) {
+    const int64_t j = base + kThreads * kQuad * q + kQuad * tid;
+    uint32_t nib = 0;
+    if (nv[q] > 0) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) nib |= (k < nv[q] ? sign_bit(x[q].v[k], p.parity) : 0u) << k;
+    }
+    const uint64_t word = wave_pack_words(nib);
+    if ((tid & 15) == 0 && j < p.ld) p.bits[i * (p.ld >> 6) + (j >> 6)] = word;
+  }
 }
 
 struct VoteParams {
-  const uint64_t* bits;  // [W][ld/64]
+  const uint64_t* bits;  // [W][words]
   uint8_t* counts;       // [d] or null
   int8_t* sign;          // [d] or null
+  uint64_t* sign_bits;   // [words] or null (bit-plane output)
+  uint64_t* zero_bits;   // [words] or null
   int64_t d, words;
   int32_t W;
   uint32_t parity;
   int32_t tie_zero;
 };
 
-// grid: ceil(d/1024); 256 threads; 4 elements per thread.
-__global__ __launch_bounds__(kThreads) void k_vote(VoteParams p) {
-  const int64_t j = (static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x) * kQuad;
-  if (j >= p.d) return;
-  const int nv = p.d - j >= 4 ? 4 : static_cast<int>(p.d - j);
-  const uint64_t* __restrict__ col = p.bits + (j >> 6);
-  const int sh = static_cast<int>(j & 63);
-  uint32_t cnt = 0;
+// Bit-sliced vertical counter: plane k holds bit k of the count of each of
+// the 64 elements of a word.  Adding one worker's word x is a ripple of
+// half-adders across the planes (two bitwise operations per plane).
+template <int NPL>
+__device__ __forceinline__ void vadd(uint64_t (&c)[NPL], uint64_t x) {
+#pragma unroll
+  for (int k = 0; k < NPL; ++k) {
+    const uint64_t carry = c[k] & x;
+    c[k] ^= x;
+    x = carry;
+  }
+}
+
+// One lane per 64-element word: loads the W workers' words of its column
+// (consecutive lanes read consecutive words: one coalesced 512-byte access
+// per wave and worker), counts the +1 bits of each element with bit-sliced
+// adders, then writes the 64 counts and signs (4 + 4 sixteen-byte stores),
+// and/or the sign planes from a bit-sliced comparison against W/2.
+template <int NPL>
+__global__ __launch_bounds__(kThreads) void k_vote_sliced(VoteParams p) {
+  const int64_t wi = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  if (wi >= p.words) return;
+  const int64_t j0 = wi << 6;
+  uint64_t c[NPL];
+#pragma unroll
+  for (int k = 0; k < NPL; ++k) c[k] = 0;
   int i = 0;
   for (; i + 8 <= p.W; i += 8) {
-    uint64_t w[8];
+    uint64_t x[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) w[u] = col[static_cast<int64_t>(i + u) * p.words];
+    for (int u = 0; u < 8; ++u) x[u] = p.bits[static_cast<int64_t>(i + u) * p.words + wi];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) cnt += nibble_to_bytes(static_cast<uint32_t>(w[u] >> sh) & 0xFu);
+    for (int u = 0; u < 8; ++u) vadd<NPL>(c, x[u]);
   }
-  for (; i < p.W; ++i)
-    cnt += nibble_to_bytes(static_cast<uint32_t>(col[static_cast<int64_t>(i) * p.words] >> sh) & 0xFu);
-  if (nv < 4) cnt &= (1u << (8 * nv)) - 1u;  // bits past d are 0 anyway
-  if (p.counts) st_b4(p.counts + j, cnt, nv);
-  if (p.sign) {
-    uint32_t packed = 0;
+  for (; i < p.W; ++i) vadd<NPL>(c, p.bits[static_cast<int64_t>(i) * p.words + wi]);
+
+  const int64_t rem = p.d - j0;  // elements of this word that exist
+  const uint64_t live = rem >= 64 ? ~0ull : (rem > 0 ? (1ull << rem) - 1ull : 0ull);
+
+  if (p.sign_bits) {
+    // gt: count > floor(W/2); eq: count == floor(W/2), a tie only for even W
+    const uint32_t K = static_cast<uint32_t>(p.W) >> 1;
+    uint64_t gt = 0, eq = ~0ull;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int twice = 2 * static_cast<int>((cnt >> (8 * k)) & 0xFFu);
-      const int s = twice > p.W ? 1 : (twice < p.W ? -1 : (p.tie_zero ? 0 : (p.parity ? 1 : -1)));
-      packed |= (static_cast<uint32_t>(s) & 0xFFu) << (8 * k);
+    for (int k = NPL - 1; k >= 0; --k) {
+      if ((K >> k) & 1u) {
+        eq &= c[k];
+      } else {
+        gt |= eq & c[k];
+        eq &= ~c[k];
+      }
     }
-    st_b4(p.sign + j, packed, nv);
+    const uint64_t tie = (p.W & 1) ? 0ull : eq;
+    const uint64_t pos = gt | ((!p.tie_zero && p.parity) ? tie : 0ull);
+    p.sign_bits[wi] = pos & live;
+    if (p.zero_bits) p.zero_bits[wi] = (p.tie_zero ? tie : 0ull) & live;
   }
+  if (p.counts || p.sign) {
+    uint32_t cw[16], sw[16];
+#pragma unroll
+    for (int g = 0; g < 16; ++g) {
+      uint32_t v = 0;
+#pragma unroll
+      for (int k = 0; k < NPL; ++k)
+        v += nibble_to_bytes(static_cast<uint32_t>(c[k] >> (4 * g)) & 0xFu) << k;
+      cw[g] = v;
+      uint32_t s4 = 0;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int twice = 2 * static_cast<int>((v >> (8 * b)) & 0xFFu);
+        const int s = twice > p.W ? 1 : (twice < p.W ? -1 : (p.tie_zero ? 0 : (p.parity ? 1 : -1)));
+        s4 |= (static_cast<uint32_t>(s) & 0xFFu) << (8 * b);
+      }
+      sw[g] = s4;
+    }
+    if (rem >= 64) {
+      if (p.counts) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          *reinterpret_cast<uint4*>(p.counts + j0 + 16 * q) =
+              make_uint4(cw[4 * q], cw[4 * q + 1], cw[4 * q + 2], cw[4 * q + 3]);
+      }
+      if (p.sign) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          *reinterpret_cast<uint4*>(p.sign + j0 + 16 * q) =
+              make_uint4(sw[4 * q], sw[4 * q + 1], sw[4 * q + 2], sw[4 * q + 3]);
+      }
+    } else {
+      for (int e = 0; e < rem; ++e) {
+        const int g = e >> 2, b = e & 3;
+        if (p.counts) p.counts[j0 + e] = static_cast<uint8_t>(cw[g] >> (8 * b));
+        if (p.sign) p.sign[j0 + e] = static_cast<int8_t>(sw[g] >> (8 * b));
+      }
+    }
+  }
+}
+
+// Number of bit planes that hold counts up to W.
+static int planes_for(int W) {
+  int k = 0;
+  while ((1 << k) <= W) ++k;
+  return k;
+}
+
+static hipError_t launch_vote_sliced(const VoteParams& p, hipStream_t st) {
+  const int64_t grid = (p.words + kThreads - 1) / kThreads;
+  const dim3 g(static_cast<unsigned>(grid)), b(kThreads);
+  const int npl = planes_for(p.W);
+  if (npl <= 1) hipLaunchKernelGGL(k_vote_sliced<1>, g, b, 0, st, p);
+  else if (npl == 2) hipLaunchKernelGGL(k_vote_sliced<2>, g, b, 0, st, p);
+  else if (npl == 3) hipLaunchKernelGGL(k_vote_sliced<3>, g, b, 0, st, p);
+  else if (npl == 4) hipLaunchKernelGGL(k_vote_sliced<4>, g, b, 0, st, p);
+  else if (npl == 5) hipLaunchKernelGGL(k_vote_sliced<5>, g, b, 0, st, p);
+  else if (npl == 6) hipLaunchKernelGGL(k_vote_sliced<6>, g, b, 0, st, p);
+  else if (npl == 7) hipLaunchKernelGGL(k_vote_sliced<7>, g, b, 0, st, p);
+  else hipLaunchKernelGGL(k_vote_sliced<8>, g, b, 0, st, p);
+  return hipGetLastError();
 }
 
 hipError_t launch_pack(const float* x, uint64_t* bits, int64_t d, int64_t ld, int W,
                        uint32_t parity, hipStream_t st) {
   PackParams p{x, bits, d, ld, parity};
-  const dim3 grid(static_cast<unsigned>((ld + kThreads * kQuad - 1) / (kThreads * kQuad)),
-                  static_cast<unsigned>(W));
+  const dim3 grid(static_cast<unsigned>((ld + kBlock - 1) / kBlock), static_cast<unsigned>(W));
   hipLaunchKernelGGL(k_pack, grid, dim3(kThreads), 0, st, p);
   return hipGetLastError();
 }
 
 hipError_t launch_vote(const uint64_t* bits, uint8_t* counts, int8_t* sign, int64_t d, int64_t ld,
                        int W, uint32_t parity, int tie_zero, hipStream_t st) {
-  VoteParams p{bits, counts, sign, d, ld >> 6, W, parity, tie_zero};
-  const int64_t grid = (d + kThreads * kQuad - 1) / (kThreads * kQuad);
-  hipLaunchKernelGGL(k_vote, dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, st, p);
-  return hipGetLastError();
+  VoteParams p{bits, counts, sign, nullptr, nullptr, d, ld >> 6, W, parity, tie_zero};
+  return launch_vote_sliced(p, st);
+}
+
+hipError_t launch_vote_bits(const uint64_t* bits, uint64_t* sign_bits, uint64_t* zero_bits,
+                            int64_t d, int64_t ld, int W, uint32_t parity, int tie_zero,
+                            hipStream_t st) {
+  VoteParams p{bits, nullptr, nullptr, sign_bits, zero_bits, d, ld >> 6, W, parity, tie_zero};
+  return launch_vote_sliced(p, st);
 }
 
 }  // namespace lioncub

@@ -9,66 +9,17 @@
 // the referee report on summation width).  These kernels are the per-GPU
 // halves of that exchange, so the single-GPU pieces compose into it:
 //
-//   vote_bits:  W bitmaps -> the global sign as bit planes (sign, zero)
 //   pack_codes: int8 codes -> n-bit two's complement fields, 32 elements per
 //               group of n 32-bit words
 //   unpack_sum: W packed rows -> int32 sums and their signs
 //
-// (Applying a global sign bitmap to theta and the momenta is a mode of the
-// fused step kernel.)
+// (The global sign of the vote as bit planes comes from the bit-sliced vote
+// kernel; applying a global sign bitmap to theta and the momenta is a mode of
+// the fused step kernel.)
 #include "device.hpp"
 #include "layout.hpp"
 
 namespace lioncub {
-
-struct VoteBitsParams {
-  const uint64_t* bits;  // [W][words]
-  uint64_t* sign_bits;   // [words]
-  uint64_t* zero_bits;   // [words] or null
-  int64_t d, words;
-  int32_t W;
-  uint32_t parity;
-  int32_t tie_zero;
-};
-
-// grid: ceil(ld/1024); 256 threads, a quad of elements per thread; counts in
-// four byte lanes of one register, planes assembled by wave ballots.
-__global__ __launch_bounds__(kThreads) void k_vote_bits(VoteBitsParams p) {
-  const int tid = threadIdx.x;
-  const int64_t j = (static_cast<int64_t>(blockIdx.x) * kThreads + tid) * kQuad;
-  const int64_t rem = p.d - j;
-  const int nv = rem >= 4 ? 4 : (rem > 0 ? static_cast<int>(rem) : 0);
-  uint32_t pos = 0, zer = 0;
-  if (nv > 0) {
-    const uint64_t* __restrict__ col = p.bits + (j >> 6);
-    const int sh = static_cast<int>(j & 63);
-    uint32_t cnt = 0;
-    int i = 0;
-    for (; i + 8 <= p.W; i += 8) {
-      uint64_t w[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) w[u] = col[static_cast<int64_t>(i + u) * p.words];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) cnt += nibble_to_bytes(static_cast<uint32_t>(w[u] >> sh) & 0xFu);
-    }
-    for (; i < p.W; ++i)
-      cnt += nibble_to_bytes(static_cast<uint32_t>(col[static_cast<int64_t>(i) * p.words] >> sh) & 0xFu);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      if (k >= nv) break;
-      const int twice = 2 * static_cast<int>((cnt >> (8 * k)) & 0xFFu);
-      const int s = twice > p.W ? 1 : (twice < p.W ? -1 : (p.tie_zero ? 0 : (p.parity ? 1 : -1)));
-      pos |= (s > 0 ? 1u : 0u) << k;
-      zer |= (s == 0 ? 1u : 0u) << k;
-    }
-  }
-  const uint64_t wpos = wave_pack_words(pos);
-  const uint64_t wzer = wave_pack_words(zer);
-  if ((tid & 15) == 0 && (j >> 6) < p.words) {
-    p.sign_bits[j >> 6] = wpos;
-    if (p.zero_bits) p.zero_bits[j >> 6] = wzer;
-  }
-}
 
 struct WireParams {
   const int8_t* codes;   // [W][ld]
@@ -165,15 +116,6 @@ __global__ __launch_bounds__(kThreads) void k_unpack_sum(WireParams p) {
       if (p.sign) p.sign[j0 + k] = static_cast<int8_t>((S[k] > 0) - (S[k] < 0));
     }
   }
-}
-
-hipError_t launch_vote_bits(const uint64_t* bits, uint64_t* sign_bits, uint64_t* zero_bits,
-                            int64_t d, int64_t ld, int W, uint32_t parity, int tie_zero,
-                            hipStream_t st) {
-  VoteBitsParams p{bits, sign_bits, zero_bits, d, ld >> 6, W, parity, tie_zero};
-  const int64_t grid = (ld + kThreads * kQuad - 1) / (kThreads * kQuad);
-  hipLaunchKernelGGL(k_vote_bits, dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, st, p);
-  return hipGetLastError();
 }
 
 hipError_t launch_pack_codes(const int8_t* codes, uint32_t* wire, int64_t d, int64_t ld, int W,
