@@ -241,6 +241,38 @@ void lco_m1_all(const lco_cfg *cfg, int64_t ld, const float *m, const void *g,
   free(c);
 }
 
+/* Diagnostics of one column ([LC] Figure 4 and Figure 11: whether the
+ * quantised update's sign matches or flips the sign of the unquantised one;
+ * the reference-graph note on majority-vote ties; Figure 6: the spread of
+ * the workers' momenta).  The unquantised aggregate is sum_i c_i in fp32,
+ * summed in worker order; the momentum variance is S2/W - (S1/W)^2 with S1,
+ * S2 the fp64 sums of m'_i and m'_i*m'_i in worker order, floored at 0. */
+static void lco_column_stats(const lco_cfg *cfg, int32_t T, int32_t count, int8_t s,
+                             float csum, const float *mcol, int64_t ldc,
+                             const lco_debug *dbg) {
+  const int32_t W = cfg->W;
+  if (dbg->stats) {
+    uint64_t *st = dbg->stats + 4 * (int64_t)T;
+    int ref = (csum > 0.0f) - (csum < 0.0f);
+    if (cfg->agg != LCO_AGG_L1SUM && 2 * count == W) st[0] += 1;
+    if (s != 0 && s == ref) st[1] += 1;
+    if (s != 0 && s == -ref) st[2] += 1;
+    if (s == 0) st[3] += 1;
+  }
+  if (dbg->mvar_max) {
+    double S1 = 0.0, S2 = 0.0;
+    for (int32_t i = 0; i < W; i++) {
+      double v = (double)mcol[i * ldc];
+      S1 = S1 + v;
+      S2 = S2 + (v * v);
+    }
+    double mean = S1 / (double)W;
+    double var = (S2 / (double)W) - (mean * mean);
+    if (var < 0.0) var = 0.0;
+    if (var > dbg->mvar_max[T]) dbg->mvar_max[T] = var;
+  }
+}
+
 /* One element column j: every worker's c from the pre-step m, compression,
  * aggregation, the global sign applied to theta (decoupled weight decay, the
  * Lion rule), then each worker's momentum update and, on averaging steps for
@@ -266,9 +298,11 @@ void lco_step_range(const lco_cfg *cfg, int64_t j0, int64_t j1,
 
     /* 1-2: c per worker, compressed; 3: aggregated */
     int32_t count = 0, sum = 0;
+    float csum = 0.0f;
     for (int32_t i = 0; i < W; i++) {
       float G = load_g(cfg, g, i * ldc + col);
       float c = (cfg->beta1 * m[i * ldc + col]) + (omega1 * G);
+      csum = i == 0 ? c : csum + c;
       if (cfg->agg != LCO_AGG_L1SUM) {
         int b = lco_bit(c, t);
         count += b;
@@ -320,6 +354,8 @@ void lco_step_range(const lco_cfg *cfg, int64_t j0, int64_t j1,
       float G = load_g(cfg, g, i * ldc + col);
       m[i * ldc + col] = (cfg->beta2 * m[i * ldc + col]) + (omega2 * G);
     }
+    if (dbg && (dbg->stats || dbg->mvar_max))
+      lco_column_stats(cfg, T, count, s, csum, m + col, ldc, dbg);
     if (avg_step && cfg->sync_m && cfg->sync_m[T]) {
       float acc = m[col];
       for (int32_t i = 1; i < W; i++) acc = acc + m[i * ldc + col];

@@ -122,6 +122,15 @@ typedef struct {
   uint8_t  *counts; /* [j1-j0]                                           */
   int32_t  *sums;   /* [j1-j0]                                           */
   int8_t   *sign;   /* [j1-j0]                                           */
+  /* Per-tensor diagnostics, accumulated (the caller zeroes them):
+   * stats[T][0] ties (2*count == W, vote and averaging paths),
+   * stats[T][1] match: applied sign == sgn(sum_i c_i) != 0,
+   * stats[T][2] flip:  applied sign == -sgn(sum_i c_i) != 0,
+   * stats[T][3] zero:  applied sign == 0;
+   * mvar_max[T] = max over the tensor's elements of the inter-worker
+   * variance of the new momenta (before any averaging). */
+  uint64_t *stats;    /* [n_tensors][4] */
+  double   *mvar_max; /* [n_tensors]    */
 } lco_debug;
 
 /* One step over the element range [j0, j1).  Chunk layout: element j of

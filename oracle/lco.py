@@ -28,7 +28,8 @@ class Cfg(C.Structure):
 
 class Debug(C.Structure):
     _fields_ = [("bits", C.c_void_p), ("codes", C.c_void_p), ("counts", C.c_void_p),
-                ("sums", C.c_void_p), ("sign", C.c_void_p)]
+                ("sums", C.c_void_p), ("sign", C.c_void_p), ("stats", C.c_void_p),
+                ("mvar_max", C.c_void_p)]
 
 
 _lib = None
@@ -203,9 +204,11 @@ def _debug_arrays(wl, ncols, ldc, want):
         "counts": np.zeros(ncols, dtype=np.uint8),
         "sums": np.zeros(ncols, dtype=np.int32),
         "sign": np.zeros(ncols, dtype=np.int8),
+        "stats": np.zeros((wl.n_tensors, 4), dtype=np.uint64),
+        "mvar_max": np.zeros(wl.n_tensors, dtype=np.float64),
     }
     dbg = Debug(*(None if arr[k] is None else arr[k].ctypes.data for k in
-                  ("bits", "codes", "counts", "sums", "sign")))
+                  ("bits", "codes", "counts", "sums", "sign", "stats", "mvar_max")))
     return dbg, arr
 
 

@@ -616,3 +616,63 @@ def test_avg_aggregation_values(oracle):
         assert np.array_equal(theta, -want)        # theta' = 0 - 1*(s + 0)
         assert np.array_equal(dbg["sign"], np.sign(2 * v - W).astype(np.int8))
     assert np.float32(float(Fraction(1, 3))) == np.float32(0.33333334)
+
+
+# ------------------------------------------------------ diagnostics (f3) --
+
+def test_stats_ties_by_construction(oracle):
+    """W = 4, columns built with a known number of +1 signs: the tie counter
+    equals the number of columns built with exactly two (both parities)."""
+    W = 4
+    rs = np.random.default_rng(21)
+    npos = rs.integers(0, W + 1, 300)
+    d = npos.size
+    wl = wls.Workload(name="st", tensors=[("a", 128), ("b", d - 128)], W=W, beta1=0.5)
+    g = np.zeros((W, wl.ld), np.float32)
+    for j, k in enumerate(npos):
+        col = np.array([1.0] * k + [-1.0] * (W - k), np.float32)
+        g[:, j] = rs.permutation(col)
+    for t in (1, 2):
+        theta = np.zeros(d, np.float32)
+        m = np.zeros((W, wl.ld), np.float32)
+        dbg = oracle.step(wl, theta, m, g, t, debug=True)
+        assert dbg["stats"][0, 0] == np.count_nonzero(npos[:128] == 2)
+        assert dbg["stats"][1, 0] == np.count_nonzero(npos[128:] == 2)
+        # with the parity tie rule no applied sign is 0, and sgn(sum c) = sgn(2k - W)
+        assert dbg["stats"][:, 3].sum() == 0
+        assert dbg["stats"][:, 1].sum() == np.count_nonzero(npos != 2)
+
+
+def test_stats_match_flip_handworked(oracle):
+    """W = 3, n = 2, one tensor of 4 elements, c = g/2 (beta1 = 0.5, m = 0):
+      w0 = w1 = [0.5, 0.25, 0.25, 0]: M1 = 0.25, codes [1, 1, 1, 0]
+      w2 = [-3, 3, 3, 3]:             M1 = 3,    codes [-1, 1, 1, 1]
+    sums [1, 3, 3, 1] -> signs all +1; sum of c [-2, 3.5, 3.5, 3] -> column 0
+    flips, columns 1-3 match."""
+    wl = wls.flat("mf", 4, W=3, agg="l1", qbits=2, beta1=0.5)
+    g = np.zeros((3, 64), np.float32)
+    g[0, :4] = g[1, :4] = np.array([0.5, 0.25, 0.25, 0.0]) * 2
+    g[2, :4] = np.array([-3.0, 3.0, 3.0, 3.0]) * 2
+    dbg = oracle.step(wl, np.zeros(4, np.float32), np.zeros((3, 64), np.float32), g, 1, debug=True)
+    assert dbg["sums"].tolist() == [1, 3, 3, 1]
+    assert dbg["stats"][0].tolist() == [0, 3, 1, 0]
+
+
+def test_stats_momentum_variance_exact(oracle):
+    """beta2 = 0.5, m = 0 and small-integer gradients make every new momentum
+    exact (g/2), and the fp64 sums exact, so the largest inter-worker
+    variance per tensor equals the exact population variance."""
+    W = 5
+    rs = np.random.default_rng(4)
+    wl = wls.Workload(name="mv", tensors=[("a", 64), ("b", 192)], W=W, beta2=0.5)
+    g = np.zeros((W, wl.ld), np.float32)
+    g[:, : wl.d] = rs.integers(-20, 21, (W, wl.d))
+    dbg = oracle.step(wl, np.zeros(wl.d, np.float32), np.zeros((W, wl.ld), np.float32), g, 1,
+                      debug=True)
+    for T, (a, b) in enumerate([(0, 64), (64, 256)]):
+        best = Fraction(0)
+        for j in range(a, b):
+            vals = [Fraction(int(g[i, j]), 2) for i in range(W)]
+            mean = sum(vals) / W
+            best = max(best, sum((v - mean) ** 2 for v in vals) / W)
+        assert dbg["mvar_max"][T] == float(best)
