@@ -17,9 +17,9 @@ F32, BF16 = 0, 1
 AGG_VOTE, AGG_L1SUM, AGG_AVG = 0, 1, 2
 TIE_PARITY, TIE_ZERO = 0, 1
 (K_VOTE_STEP, K_M1_PARTIAL, K_M1_FINALIZE, K_L1_STEP, K_PACK, K_VOTE, K_QUANT, K_VOTE_BITS,
- K_APPLY, K_PACK_CODES, K_UNPACK_SUM, K_AVG_STEP, K_COUNT) = range(13)
+ K_APPLY, K_PACK_CODES, K_UNPACK_SUM, K_AVG_STEP, K_STATS, K_COUNT) = range(14)
 KERNEL_NAMES = ["vote_step", "m1_partial", "m1_finalize", "l1_step", "pack", "vote", "quant",
-                "vote_bits", "apply", "pack_codes", "unpack_sum", "avg_step"]
+                "vote_bits", "apply", "pack_codes", "unpack_sum", "avg_step", "stats"]
 
 EXPORTS = ["lioncub_workspace_bytes", "lioncub_init", "lioncub_set_stream", "lioncub_step",
            "lioncub_pack", "lioncub_vote", "lioncub_quant_l1", "lioncub_vote_bits",
@@ -39,7 +39,8 @@ class lioncub_config(C.Structure):
 
 class lioncub_debug(C.Structure):
     _fields_ = [("bits", C.c_void_p), ("codes", C.c_void_p), ("counts", C.c_void_p),
-                ("sums", C.c_void_p), ("sign", C.c_void_p), ("m1", C.c_void_p)]
+                ("sums", C.c_void_p), ("sign", C.c_void_p), ("m1", C.c_void_p),
+                ("stats", C.c_void_p), ("mvar_max", C.c_void_p)]
 
 
 _lib = None
@@ -151,7 +152,8 @@ def lioncub_step(ctx, theta, m, g, t, dbg=None):
     d = None
     if dbg is not None:
         d = lioncub_debug(*(None if dbg.get(k) is None else dbg[k].data_ptr()
-                            for k in ("bits", "codes", "counts", "sums", "sign", "m1")))
+                            for k in ("bits", "codes", "counts", "sums", "sign", "m1",
+                                      "stats", "mvar_max")))
     _check("lioncub_step", lib().lioncub_step(ctx, _ptr(theta), _ptr(m), _ptr(g), int(t),
                                               C.byref(d) if d is not None else None))
 

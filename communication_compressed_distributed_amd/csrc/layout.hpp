@@ -68,7 +68,13 @@ struct StepParams {
   uint8_t* counts;
   int32_t* sums;
   int8_t* sign;
+  // diagnostics: per-block partials [nblk][kStat] (workspace), then per tensor
+  uint64_t* bstat;
+  uint64_t* stats;     // [nT][4]: ties, sign matches, flips, zero signs
+  double* mvar_max;    // [nT]: largest inter-worker variance of the new momenta
 };
+
+constexpr int kStat = 8;  // per-block diagnostic slots: 4 counters, variance bits, pad
 
 struct M1Params {
   const BlockEnt* blk;

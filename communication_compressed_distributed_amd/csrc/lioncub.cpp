@@ -18,6 +18,7 @@ hipError_t launch_step(const StepParams& p, int nblk, int theta_bf16, int grad_b
                        hipStream_t st);
 hipError_t launch_zero_tail_words(uint64_t* bits, int64_t words, int64_t first, int W,
                                   hipStream_t st);
+hipError_t launch_stats_reduce(const StepParams& p, int nT, hipStream_t st);
 hipError_t launch_m1(const M1Params& p, int src_x, int grad_bf16, hipStream_t st);
 hipError_t launch_m1_finalize(const M1Params& p, hipStream_t st);
 hipError_t launch_quant_codes(const M1Params& p, int8_t* codes, hipStream_t st);
@@ -41,7 +42,7 @@ namespace {
 constexpr size_t kWsAlign = 256;
 
 struct WsLayout {
-  size_t blk, tens, grp, partial, gval, m1, scale, total;
+  size_t blk, tens, grp, partial, gval, m1, scale, bstat, total;
 };
 
 size_t align_up(size_t x) { return (x + kWsAlign - 1) / kWsAlign * kWsAlign; }
@@ -63,6 +64,8 @@ WsLayout ws_layout(int64_t nblk, int64_t ngrp, int64_t nT, int64_t W) {
   o = align_up(o + static_cast<size_t>(W * nT) * sizeof(double));
   L.scale = o;
   o = align_up(o + static_cast<size_t>(W * nT) * sizeof(double));
+  L.bstat = o;
+  o = align_up(o + static_cast<size_t>(nblk) * kStat * sizeof(uint64_t));
   L.total = o;
   return L;
 }
@@ -118,6 +121,7 @@ struct lioncub_ctx {
   double* gval;
   double* m1;
   double* scale;
+  uint64_t* bstat;
   std::vector<BlockEnt> h_blk;
   std::vector<TensorEnt> h_tens;
   std::vector<GroupEnt> h_grp;
@@ -151,6 +155,7 @@ void fill_step_params(const lioncub_ctx* c, StepParams* p) {
   p->blk = c->blk;
   p->tens = c->tens;
   p->scale = c->scale;
+  p->bstat = c->bstat;
   p->ld = c->cfg.ld;
   p->W = c->cfg.W;
   p->nT = c->cfg.n_tensors;
@@ -224,6 +229,7 @@ int lioncub_init(lioncub_ctx** out, const lioncub_config* cfg, void* hip_stream,
   c->gval = reinterpret_cast<double*>(ws + L.gval);
   c->m1 = reinterpret_cast<double*>(ws + L.m1);
   c->scale = reinterpret_cast<double*>(ws + L.scale);
+  c->bstat = reinterpret_cast<uint64_t*>(ws + L.bstat);
 
   c->h_tens.resize(cfg->n_tensors);
   c->h_blk.reserve(nblk);
@@ -301,13 +307,16 @@ int lioncub_step(lioncub_ctx* ctx, void* theta, float* m, const void* g, int64_t
     if ((dbg->bits || dbg->counts) && l1) return LIONCUB_EINVAL;
     if ((dbg->codes || dbg->sums || dbg->m1) && !l1) return LIONCUB_EINVAL;
     if (!aligned(dbg->bits, 16) || !aligned(dbg->codes, 16) || !aligned(dbg->counts, 16) ||
-        !aligned(dbg->sums, 16) || !aligned(dbg->sign, 16) || !aligned(dbg->m1, 16))
+        !aligned(dbg->sums, 16) || !aligned(dbg->sign, 16) || !aligned(dbg->m1, 16) ||
+        !aligned(dbg->stats, 16) || !aligned(dbg->mvar_max, 16))
       return LIONCUB_EALIGN;
     p.bits = dbg->bits;
     p.codes = dbg->codes;
     p.counts = dbg->counts;
     p.sums = dbg->sums;
     p.sign = dbg->sign;
+    p.stats = dbg->stats;
+    p.mvar_max = dbg->mvar_max;
   }
   hipError_t e = hipSuccess;
   if (l1) {
@@ -326,6 +335,8 @@ int lioncub_step(lioncub_ctx* ctx, void* theta, float* m, const void* g, int64_t
     });
   if (e == hipSuccess && p.bits)
     e = launch_zero_tail_words(p.bits, cf.ld / 64, (cf.d + 63) / 64, cf.W, ctx->stream);
+  if (e == hipSuccess && (p.stats || p.mvar_max))
+    e = run(ctx, LIONCUB_K_STATS, [&] { return launch_stats_reduce(p, cf.n_tensors, ctx->stream); });
   return dev_status(e);
 }
 

@@ -29,6 +29,79 @@
 
 namespace lioncub {
 
+// Sum the workgroup's diagnostic counters and take its largest variance;
+// thread 0 writes them to the block's slots (no atomics: a second kernel
+// folds the blocks of each tensor in order).
+__device__ __forceinline__ void block_stats(const StepParams& p, unsigned tie, unsigned match,
+                                         unsigned flip, unsigned zero, double var) {
+  __shared__ unsigned sh_c[4][4];
+  __shared__ double sh_v[4];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int s = 32; s >= 1; s >>= 1) {
+    tie += __shfl_xor(tie, s, kWave);
+    match += __shfl_xor(match, s, kWave);
+    flip += __shfl_xor(flip, s, kWave);
+    zero += __shfl_xor(zero, s, kWave);
+    var = fmax(var, __shfl_xor(var, s, kWave));
+  }
+  if (lane == 0) {
+    sh_c[wave][0] = tie;
+    sh_c[wave][1] = match;
+    sh_c[wave][2] = flip;
+    sh_c[wave][3] = zero;
+    sh_v[wave] = var;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint64_t* out = p.bstat + static_cast<int64_t>(blockIdx.x) * kStat;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      out[k] = static_cast<uint64_t>(sh_c[0][k]) + sh_c[1][k] + sh_c[2][k] + sh_c[3][k];
+    const double v = fmax(fmax(sh_v[0], sh_v[1]), fmax(sh_v[2], sh_v[3]));
+    out[4] = static_cast<uint64_t>(__double_as_longlong(v));
+  }
+}
+
+// One workgroup per tensor: fold its blocks' diagnostic slots.
+__global__ __launch_bounds__(kThreads) void k_stats_reduce(StepParams p) {
+  __shared__ uint64_t sh_c[kThreads][4];
+  __shared__ double sh_v[kThreads];
+  const int T = blockIdx.x, tid = threadIdx.x;
+  const TensorEnt te = p.tens[T];
+  uint64_t c[4] = {0, 0, 0, 0};
+  double v = 0.0;
+  for (int b = te.blk0 + tid; b < te.blk0 + te.nblk; b += kThreads) {
+    const uint64_t* in = p.bstat + static_cast<int64_t>(b) * kStat;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) c[k] += in[k];
+    v = fmax(v, __longlong_as_double(static_cast<long long>(in[4])));
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) sh_c[tid][k] = c[k];
+  sh_v[tid] = v;
+  __syncthreads();
+  if (tid == 0) {
+    uint64_t tot[4] = {0, 0, 0, 0};
+    double mx = 0.0;
+    for (int u = 0; u < kThreads; ++u) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) tot[k] += sh_c[u][k];
+      mx = fmax(mx, sh_v[u]);
+    }
+    if (p.stats) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) p.stats[static_cast<int64_t>(T) * 4 + k] = tot[k];
+    }
+    if (p.mvar_max) p.mvar_max[T] = mx;
+  }
+}
+
+hipError_t launch_stats_reduce(const StepParams& p, int nT, hipStream_t st) {
+  hipLaunchKernelGGL(k_stats_reduce, dim3(nT), dim3(kThreads), 0, st, p);
+  return hipGetLastError();
+}
+
 // One workgroup, one block.  Each thread owns the quads j[q] = start +
 // 1024*q + 4*tid (q = 0..3) and walks the workers in the outer loop, so each
 // worker row is read as one 16 KB contiguous run per workgroup before the
@@ -62,6 +135,18 @@ __device__ __forceinline__ void step_block(const StepParams& p, const BlockEnt& 
   uint32_t cnt[Q];    // vote: per-element counts, one byte each
   int sum[Q][4];      // L1: per-element integer sums
   F4 acc[Q];          // averaging: running sum of new momenta
+  // diagnostics (debug instantiations): unquantised sum of c in worker order,
+  // fp64 sums of the new momenta and of their squares
+  constexpr bool ST = DBG && AGG != kAggApply;
+  const bool want_st = ST && (p.stats || p.mvar_max);
+  float csum[ST ? Q : 1][4];
+  double s1[ST ? Q : 1][4], s2[ST ? Q : 1][4];
+  if constexpr (ST) {
+#pragma unroll
+    for (int q = 0; q < Q; ++q)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) csum[q][k] = 0.0f, s1[q][k] = 0.0, s2[q][k] = 0.0;
+  }
 #pragma unroll
   for (int q = 0; q < Q; ++q) {
     cnt[q] = 0;
@@ -125,6 +210,14 @@ __device__ __forceinline__ void step_block(const StepParams& p, const BlockEnt& 
             if (DBG) nib |= (static_cast<uint32_t>(qc) & 0xFFu) << (8 * k);
           }
           mn.v[k] = (p.beta2 * mv[b][q].v[k]) + (p.omega2 * gv[b][q].v[k]);
+          if constexpr (ST) {
+            if (want_st) {
+              csum[q][k] = i == 0 ? c : csum[q][k] + c;
+              const double v = static_cast<double>(mn.v[k]);
+              s1[q][k] = s1[q][k] + v;
+              s2[q][k] = s2[q][k] + (v * v);
+            }
+          }
         }
         if (AGG == kAggVote || AGG == kAggAvg) {
           cnt[q] += nibble_to_bytes(nib);
@@ -150,6 +243,8 @@ __device__ __forceinline__ void step_block(const StepParams& p, const BlockEnt& 
     }
   }
 
+  unsigned st_tie = 0, st_match = 0, st_flip = 0, st_zero = 0;
+  double st_var = 0.0;
 #pragma unroll
   for (int q = 0; q < Q; ++q) {
     if (!FULL && nv[q] == 0) continue;
@@ -192,6 +287,23 @@ __device__ __forceinline__ void step_block(const StepParams& p, const BlockEnt& 
         sf[k] = static_cast<float>(s[k]);
       }
     }
+    if constexpr (ST) {
+      if (want_st) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          if (!FULL && k >= nv[q]) break;
+          const int ref = (csum[q][k] > 0.0f) - (csum[q][k] < 0.0f);
+          if (AGG != kAggL1 && 2 * static_cast<int>((cnt[q] >> (8 * k)) & 0xFFu) == W) st_tie++;
+          if (s[k] != 0 && s[k] == ref) st_match++;
+          if (s[k] != 0 && s[k] == -ref) st_flip++;
+          if (s[k] == 0) st_zero++;
+          const double mean = s1[q][k] / static_cast<double>(W);
+          double var = (s2[q][k] / static_cast<double>(W)) - (mean * mean);
+          if (var < 0.0) var = 0.0;
+          st_var = fmax(st_var, var);
+        }
+      }
+    }
     if (DBG && p.sign) {
       const uint32_t packed = (static_cast<uint32_t>(s[0]) & 0xFFu) |
                               ((static_cast<uint32_t>(s[1]) & 0xFFu) << 8) |
@@ -215,6 +327,9 @@ __device__ __forceinline__ void step_block(const StepParams& p, const BlockEnt& 
       for (int i = 0; i < W; ++i)
         stnt_f32x4(m + static_cast<int64_t>(i) * p.ld + j[q], acc[q], nv[q]);
     }
+  }
+  if constexpr (ST) {
+    if (want_st) block_stats(p, st_tie, st_match, st_flip, st_zero, st_var);
   }
 }
 
@@ -260,13 +375,15 @@ static hipError_t launch_t(const StepParams& p, int nblk, hipStream_t st) {
       return hipGetLastError();
     }
   }
-  hipLaunchKernelGGL((k_step<TT, GT, DBG, AGG, kWB, 0>), g, b, 0, st, p);
+  // debug outputs and diagnostics keep many more values live: one worker per
+  // batch keeps them in registers
+  hipLaunchKernelGGL((k_step<TT, GT, DBG, AGG, DBG ? 1 : kWB, 0>), g, b, 0, st, p);
   return hipGetLastError();
 }
 
 hipError_t launch_step(const StepParams& p, int nblk, int theta_bf16, int grad_bf16, int agg,
                        hipStream_t st) {
-  const bool dbg = p.bits || p.codes || p.counts || p.sums || p.sign;
+  const bool dbg = p.bits || p.codes || p.counts || p.sums || p.sign || p.stats || p.mvar_max;
   const int key = (theta_bf16 << 4) | (grad_bf16 << 3) | ((dbg ? 1 : 0) << 2) | agg;
   switch (key) {
 #define LC_CASE(TT, GT, D, A) \

@@ -104,6 +104,17 @@ typedef struct {
   int8_t *sign;    /* device [d]: the global sign applied, in {-1, 0, +1}       */
   double *m1;      /* device [W][n_tensors]: mean |c| per (worker, tensor)
                       (L1 path); does not change which step kernel runs     */
+  /* Per-tensor diagnostics of this step (written, not accumulated).
+   * Sources: the Lion Cub page's Figure 4 / Figure 11 (does the quantised
+   * update's sign match or flip the unquantised one), its note on majority
+   * ties, and Figure 6 (spread of the workers' momenta).                  */
+  uint64_t *stats; /* device [n_tensors][4]: ties (2*count == W, vote and
+                      averaging paths), matches (applied sign == sgn of the
+                      fp32 worker-order sum of c, nonzero), flips (== minus
+                      it, nonzero), zero applied signs                        */
+  double *mvar_max; /* device [n_tensors]: largest inter-worker variance of
+                      the new momenta, S2/W - (S1/W)^2 with fp64 worker-order
+                      sums S1, S2 of m' and m'^2, floored at 0                */
 } lioncub_debug;
 
 /* Bytes of device workspace lioncub_init needs for cfg (0 if cfg is invalid).
@@ -214,7 +225,8 @@ enum {
   LIONCUB_K_PACK_CODES = 9,
   LIONCUB_K_UNPACK_SUM = 10,
   LIONCUB_K_AVG_STEP = 11,
-  LIONCUB_K_COUNT = 12
+  LIONCUB_K_STATS = 12,
+  LIONCUB_K_COUNT = 13
 };
 int lioncub_profile_begin(lioncub_ctx *ctx, int32_t capacity);
 int lioncub_profile_end(lioncub_ctx *ctx, double *ms_total, int32_t *launches);

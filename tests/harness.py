@@ -98,7 +98,10 @@ def gpu_step_vs_oracle(wl, steps=2, t0=1, zeros=True, debug=True, seed_shift=0):
         d_g = to_dev(g, gb)
         dbg = None
         if debug:
-            dbg = {"sign": torch.zeros(wl.d, dtype=torch.int8, device="cuda")}
+            dbg = {"sign": torch.zeros(wl.d, dtype=torch.int8, device="cuda"),
+                   "stats": torch.full((wl.n_tensors, 4), -1, dtype=torch.int64, device="cuda"),
+                   "mvar_max": torch.full((wl.n_tensors,), -1.0, dtype=torch.float64,
+                                          device="cuda")}
             if wl.agg in ("vote", "avg"):
                 dbg["bits"] = torch.full((wl.W, wl.ld // 64), -1, dtype=torch.int64, device="cuda")
                 dbg["counts"] = torch.zeros(wl.d, dtype=torch.uint8, device="cuda")
@@ -123,5 +126,9 @@ def gpu_step_vs_oracle(wl, steps=2, t0=1, zeros=True, debug=True, seed_shift=0):
                                       want["codes"][:, : wl.d]), f"codes t={t}"
                 assert np.array_equal(to_host(dbg["sums"]), want["sums"]), f"sums t={t}"
             assert np.array_equal(got_sign, want["sign"]), f"sign t={t}"
+            assert np.array_equal(to_host(dbg["stats"]).view(np.uint64), want["stats"]), \
+                f"stats t={t}: {to_host(dbg['stats'])} vs {want['stats']}"
+            assert np.array_equal(to_host(dbg["mvar_max"]).view(np.uint64),
+                                  want["mvar_max"].view(np.uint64)), f"mvar_max t={t}"
     lc.close()
     return {"d": wl.d, "W": wl.W, "steps": steps, "ties": ties, "ok": True}
