@@ -254,7 +254,7 @@ static void lco_column_stats(const lco_cfg *cfg, int32_t T, int32_t count, int8_
   if (dbg->stats) {
     uint64_t *st = dbg->stats + 4 * (int64_t)T;
     int ref = (csum > 0.0f) - (csum < 0.0f);
-    if (cfg->agg != LCO_AGG_L1SUM && 2 * count == W) st[0] += 1;
+    if ((cfg->agg == LCO_AGG_VOTE || cfg->agg == LCO_AGG_AVG) && 2 * count == W) st[0] += 1;
     if (s != 0 && s == ref) st[1] += 1;
     if (s != 0 && s == -ref) st[2] += 1;
     if (s == 0) st[3] += 1;
@@ -303,13 +303,21 @@ void lco_step_range(const lco_cfg *cfg, int64_t j0, int64_t j1,
       float G = load_g(cfg, g, i * ldc + col);
       float c = (cfg->beta1 * m[i * ldc + col]) + (omega1 * G);
       csum = i == 0 ? c : csum + c;
-      if (cfg->agg != LCO_AGG_L1SUM) {
+      if (cfg->agg == LCO_AGG_VOTE || cfg->agg == LCO_AGG_AVG) {
         int b = lco_bit(c, t);
         count += b;
         if (dbg && dbg->bits && b)
           dbg->bits[i * words + col / 64] |= (uint64_t)1 << (col % 64);
       } else {
-        int8_t q = lco_q1(c, m1[(int64_t)i * cfg->n_tensors + T], cfg->qbits);
+        int8_t q;
+        if (cfg->agg == LCO_AGG_LINFSUM) {
+          uint64_t ctr = ((uint64_t)t * (uint64_t)W + (uint64_t)i) * (uint64_t)cfg->d +
+                         (uint64_t)j;
+          q = lco_qinf(c, m1[(int64_t)i * cfg->n_tensors + T], cfg->qbits,
+                       lco_splitmix64(cfg->seed, ctr));
+        } else {
+          q = lco_q1(c, m1[(int64_t)i * cfg->n_tensors + T], cfg->qbits);
+        }
         sum += q;
         if (dbg && dbg->codes) dbg->codes[i * ldc + col] = q;
       }
@@ -363,6 +371,69 @@ void lco_step_range(const lco_cfg *cfg, int64_t j0, int64_t j1,
       for (int32_t i = 0; i < W; i++) m[i * ldc + col] = avg;
     }
   }
+}
+
+/* ------------------------------------ max-norm stochastic baseline ---- */
+
+uint64_t lco_splitmix64(uint64_t seed, uint64_t counter) {
+  uint64_t z = seed + (counter + 1u) * 0x9E3779B97F4A7C15ull;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+double lco_minf(const float *x, int64_t n) {
+  double mx = 0.0;
+  for (int64_t k = 0; k < n; k++) {
+    double a = fabs((double)x[k]);
+    if (a > mx) mx = a;
+  }
+  return mx;
+}
+
+int8_t lco_qinf(float c, double minf, int32_t qbits, uint64_t draw) {
+  int32_t qmax = (1 << (qbits - 1)) - 1;
+  if (minf == 0.0) return 0;
+  double scale = (double)qmax / minf;
+  double y = (double)c * scale;
+  double fl = floor(y);
+  double frac = y - fl;
+  double u = (double)(draw >> 11) * 0x1.0p-53;
+  double q = fl + (u < frac ? 1.0 : 0.0);
+  if (q > (double)qmax) q = (double)qmax;
+  if (q < -(double)qmax) q = -(double)qmax;
+  return (int8_t)q;
+}
+
+void lco_quant_linf(const lco_cfg *cfg, int64_t ld, const float *x, int64_t t,
+                    int8_t *codes, double *minf) {
+  for (int32_t i = 0; i < cfg->W; i++) {
+    for (int32_t T = 0; T < cfg->n_tensors; T++) {
+      int64_t a = cfg->off[T], n = cfg->off[T + 1] - cfg->off[T];
+      double M = lco_minf(x + i * ld + a, n);
+      if (minf) minf[(int64_t)i * cfg->n_tensors + T] = M;
+      for (int64_t j = a; j < a + n; j++) {
+        uint64_t ctr = ((uint64_t)t * (uint64_t)cfg->W + (uint64_t)i) * (uint64_t)cfg->d +
+                       (uint64_t)j;
+        codes[i * ld + j] = lco_qinf(x[i * ld + j], M, cfg->qbits,
+                                     lco_splitmix64(cfg->seed, ctr));
+      }
+    }
+  }
+}
+
+void lco_minf_all(const lco_cfg *cfg, int64_t ld, const float *m, const void *g,
+                  double *minf) {
+  size_t gsz = cfg->grad_bf16 ? 2 : 4;
+  float *c = (float *)malloc((size_t)(cfg->d > 0 ? cfg->d : 1) * sizeof(float));
+  for (int32_t i = 0; i < cfg->W; i++) {
+    lco_c_row(cfg, cfg->d, m + i * ld, (const char *)g + (size_t)(i * ld) * gsz, c);
+    for (int32_t T = 0; T < cfg->n_tensors; T++) {
+      int64_t a = cfg->off[T], n = cfg->off[T + 1] - cfg->off[T];
+      minf[(int64_t)i * cfg->n_tensors + T] = lco_minf(c + a, n);
+    }
+  }
+  free(c);
 }
 
 /* ------------------- receive side and wire formats of the exchange ---- */
@@ -462,9 +533,10 @@ void lco_unpack_sum(int32_t W, int64_t d, int64_t ld, int32_t qbits,
 void lco_step(const lco_cfg *cfg, int64_t ld, void *theta, float *m,
               const void *g, int64_t t, const lco_debug *dbg) {
   double *m1 = 0;
-  if (cfg->agg == LCO_AGG_L1SUM) {
+  if (cfg->agg == LCO_AGG_L1SUM || cfg->agg == LCO_AGG_LINFSUM) {
     m1 = (double *)malloc((size_t)cfg->W * cfg->n_tensors * sizeof(double));
-    lco_m1_all(cfg, ld, m, g, m1);
+    if (cfg->agg == LCO_AGG_L1SUM) lco_m1_all(cfg, ld, m, g, m1);
+    else lco_minf_all(cfg, ld, m, g, m1);
   }
   lco_step_range(cfg, 0, cfg->d, m1, theta, m, g, ld, t, dbg);
   free(m1);

@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-enum { LCO_AGG_VOTE = 0, LCO_AGG_L1SUM = 1, LCO_AGG_AVG = 2 };
+enum { LCO_AGG_VOTE = 0, LCO_AGG_L1SUM = 1, LCO_AGG_AVG = 2, LCO_AGG_LINFSUM = 3 };
 enum { LCO_TIE_PARITY = 0, LCO_TIE_ZERO = 1 };
 
 /* Block / lane constants of the fixed mean-|x| summation tree (D-M1). */
@@ -53,10 +53,11 @@ typedef struct {
   int32_t sync_every;      /* averaging on steps with t % sync_every == 0  */
   int32_t theta_bf16;      /* theta stored as bf16 (else fp32)             */
   int32_t grad_bf16;       /* g stored as bf16 (else fp32)                 */
-  int32_t agg;             /* LCO_AGG_VOTE, LCO_AGG_L1SUM or LCO_AGG_AVG   */
-  int32_t qbits;           /* n of Eq. (1), 2..8, L1 path only             */
+  int32_t agg;             /* LCO_AGG_VOTE, _L1SUM, _AVG or _LINFSUM        */
+  int32_t qbits;           /* n of Eq. (1), 2..8, L1 and max-norm paths    */
   int32_t tie_mode;        /* LCO_TIE_PARITY or LCO_TIE_ZERO, vote path    */
   float beta1, beta2, lr, wd;
+  uint64_t seed;           /* stochastic rounding of the max-norm baseline  */
 } lco_cfg;
 
 /* bf16 <-> fp32: widening is exact; narrowing rounds to nearest-even,
@@ -111,6 +112,10 @@ void lco_c_row(const lco_cfg *cfg, int64_t n, const float *m, const void *g,
 void lco_m1_partials(const lco_cfg *cfg, int64_t n, const float *m, const void *g,
                      double *P);
 
+/* max |c| of every (worker, tensor) from the full state: [W][n_tensors]. */
+void lco_minf_all(const lco_cfg *cfg, int64_t ld, const float *m, const void *g,
+                  double *minf);
+
 /* M1 of every (worker, tensor) from the full state: m1[W][n_tensors]. */
 void lco_m1_all(const lco_cfg *cfg, int64_t ld, const float *m, const void *g,
                 double *m1);
@@ -135,10 +140,40 @@ typedef struct {
 
 /* One step over the element range [j0, j1).  Chunk layout: element j of
  * worker i lives at m[i*ldc + (j-j0)], g likewise, theta at theta[j-j0].
- * m1 is m1[W][n_tensors] (L1 path; may be NULL on the vote path). */
+ * m1 is m1[W][n_tensors] (L1 path: mean |c|; max-norm path: max |c|; may be
+ * NULL on the vote and averaging paths). */
 void lco_step_range(const lco_cfg *cfg, int64_t j0, int64_t j1,
                     const double *m1, void *theta, float *m, const void *g,
                     int64_t ldc, int64_t t, const lco_debug *dbg);
+
+/* ---- max-norm (Q-infinity) stochastic quantisation: the baseline ------
+ * PARITY PARTLY UNPINNED: the pages name this quantiser as the baseline
+ * that L1 replaces (Lion Cub review, Figure 4 caption: with stochastic
+ * rounding it sends most entries to zero; the referee report on Eq. (1)
+ * says the paper's section 2 defines that stochastic rounding) but never
+ * print its formula.  Reading taken: the form of
+ * Eq. (1) with the max |x| in place of the mean |x| and stochastic rounding
+ * in place of rounding to nearest:
+ *   q = clamp(floor(y) + [u < y - floor(y)], +-Qmax),  y = (Qmax / max|x|) * x
+ * in fp64, u uniform in [0, 1) from the counter-based generator below.
+ * Pinned: the generator's published first output, exactness of max|x|,
+ * integer y (no randomness), unbiasedness E[q] = y, and the pages' claim
+ * that on heavy-tailed updates most codes become 0. */
+
+/* SplitMix64 (Steele, Lea and Flood, 2014) used as a counter-based
+ * generator: the counter-th output of the stream started at `seed`. */
+uint64_t lco_splitmix64(uint64_t seed, uint64_t counter);
+
+/* max |x| of one row of n values (exact: fp32 magnitudes, no rounding). */
+double lco_minf(const float *x, int64_t n);
+
+/* One stochastic code; `draw` is the generator output for this element. */
+int8_t lco_qinf(float c, double minf, int32_t qbits, uint64_t draw);
+
+/* Standalone max-norm quantisation of x[W][ld] for step t: element j of
+ * worker i uses the draw with counter (t*W + i)*d + j. */
+void lco_quant_linf(const lco_cfg *cfg, int64_t ld, const float *x, int64_t t,
+                    int8_t *codes, double *minf);
 
 /* ---- receive side and wire formats of the worker-sharded exchange ---- */
 

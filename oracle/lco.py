@@ -11,7 +11,7 @@ import numpy as np
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "liblco.so")
 
-VOTE, L1SUM, AVG = 0, 1, 2
+VOTE, L1SUM, AVG, LINFSUM = 0, 1, 2, 3
 TIE_PARITY, TIE_ZERO = 0, 1
 M1_BLOCK = 4096
 
@@ -23,6 +23,7 @@ class Cfg(C.Structure):
         ("sync_every", C.c_int32), ("theta_bf16", C.c_int32), ("grad_bf16", C.c_int32),
         ("agg", C.c_int32), ("qbits", C.c_int32), ("tie_mode", C.c_int32),
         ("beta1", C.c_float), ("beta2", C.c_float), ("lr", C.c_float), ("wd", C.c_float),
+        ("seed", C.c_uint64),
     ]
 
 
@@ -70,6 +71,14 @@ def lib():
         L.lco_apply.argtypes = [C.POINTER(Cfg), i64, vp, vp, vp, i64, vp, vp]
         L.lco_pack_codes.argtypes = [i32, i64, i64, i32, vp, vp]
         L.lco_unpack_sum.argtypes = [i32, i64, i64, i32, vp, vp, vp]
+        L.lco_splitmix64.argtypes = [C.c_uint64, C.c_uint64]
+        L.lco_splitmix64.restype = C.c_uint64
+        L.lco_minf.argtypes = [vp, i64]
+        L.lco_minf.restype = C.c_double
+        L.lco_qinf.argtypes = [C.c_float, C.c_double, i32, C.c_uint64]
+        L.lco_qinf.restype = C.c_int8
+        L.lco_quant_linf.argtypes = [C.POINTER(Cfg), i64, vp, i64, vp, vp]
+        L.lco_minf_all.argtypes = [C.POINTER(Cfg), i64, vp, vp, vp]
         _lib = L
     return _lib
 
@@ -97,10 +106,11 @@ class OracleCfg:
         c.sync_every = wl.sync_every
         c.theta_bf16 = 1 if wl.theta_dtype == "bf16" else 0
         c.grad_bf16 = 1 if wl.grad_dtype == "bf16" else 0
-        c.agg = {"l1": L1SUM, "avg": AVG}.get(wl.agg, VOTE)
+        c.agg = {"l1": L1SUM, "avg": AVG, "linf": LINFSUM}.get(wl.agg, VOTE)
         c.qbits = wl.qbits
         c.tie_mode = TIE_ZERO if wl.tie == "zero" else TIE_PARITY
         c.beta1, c.beta2, c.lr, c.wd = wl.beta1, wl.beta2, wl.lr, wl.wd
+        c.seed = wl.sr_seed
         self.c = c
 
     @property
@@ -165,6 +175,38 @@ def quant_l1(wl, x):
     m1v = np.empty((wl.W, wl.n_tensors), dtype=np.float64)
     lib().lco_quant_l1(cfg.ref, x.shape[1], _p(x), _p(codes), _p(m1v))
     return codes, m1v
+
+
+def splitmix64(seed, counter):
+    return lib().lco_splitmix64(int(seed) & (2**64 - 1), int(counter) & (2**64 - 1))
+
+
+def minf(x):
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    return lib().lco_minf(_p(x), x.size)
+
+
+def qinf(c, minf_v, qbits, draw):
+    return lib().lco_qinf(float(c), float(minf_v), int(qbits), int(draw) & (2**64 - 1))
+
+
+def quant_linf(wl, x, t):
+    """Max-norm stochastic codes of x[W][ld] for step t -> (codes, minf[W][nT])."""
+    cfg = OracleCfg(wl)
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    codes = np.zeros(x.shape, dtype=np.int8)
+    mv = np.empty((wl.W, wl.n_tensors), dtype=np.float64)
+    lib().lco_quant_linf(cfg.ref, x.shape[1], _p(x), int(t), _p(codes), _p(mv))
+    return codes, mv
+
+
+def minf_all(wl, m, g):
+    cfg = OracleCfg(wl)
+    m = np.ascontiguousarray(m, dtype=np.float32)
+    g = np.ascontiguousarray(g)
+    out = np.empty((wl.W, wl.n_tensors), dtype=np.float64)
+    lib().lco_minf_all(cfg.ref, m.shape[1], _p(m), _p(g), _p(out))
+    return out
 
 
 def c_row(wl, m_row, g_row):

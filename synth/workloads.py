@@ -41,8 +41,8 @@ class Workload:
     name: str
     tensors: List[tuple]              # (name, numel), concatenated in order
     W: int
-    agg: str = "vote"                 # "vote" | "l1"
-    qbits: int = 0                    # n of Eq. (1) on the L1 path
+    agg: str = "vote"                 # "vote" | "l1" | "avg" | "linf"
+    qbits: int = 0                    # n of Eq. (1) on the L1 / max-norm paths
     tie: str = "parity"               # "parity" | "zero"
     theta_dtype: str = "f32"          # "f32" | "bf16"
     grad_dtype: str = "f32"           # "f32" | "bf16"
@@ -60,6 +60,7 @@ class Workload:
     g_scale: float = 1e-3
     g_tensor_scale: Optional[tuple] = None  # (lo, hi): per-tensor log-uniform scale
     ld_pad: int = 0                   # extra elements of row padding (multiple of 64)
+    sr_seed: int = 0x5EED             # key of the stochastic-rounding generator
 
     @property
     def d(self) -> int:

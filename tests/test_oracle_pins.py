@@ -479,10 +479,10 @@ def test_majority_tie_rate(oracle, W):
 
 # ------------------------------------------------- streaming form ---------
 
-@pytest.mark.parametrize("agg", ["vote", "l1"])
+@pytest.mark.parametrize("agg", ["vote", "l1", "linf"])
 def test_chunked_step_equals_whole_step(oracle, agg):
     wl = wls.Workload(name="chunk", tensors=[("a", 4096 * 3 + 640), ("b", 64), ("c", 8192)],
-                      W=3, agg=agg, qbits=4 if agg == "l1" else 0, sync_names=("b",),
+                      W=3, agg=agg, qbits=0 if agg == "vote" else 4, sync_names=("b",),
                       grad_dtype="bf16", theta_dtype="bf16")
     from synth import gen
     theta = gen.host_theta(wl)
@@ -490,7 +490,7 @@ def test_chunked_step_equals_whole_step(oracle, agg):
     g = gen.host_g(wl, 1)
     th1, m_1 = theta.copy(), m.copy()
     oracle.step(wl, th1, m_1, g, 2)
-    m1v = oracle.m1_all(wl, m, g) if agg == "l1" else None
+    m1v = {"l1": oracle.m1_all, "linf": oracle.minf_all}.get(agg, lambda *a: None)(wl, m, g)
     th2, m_2 = theta.copy(), m.copy()
     edges = [0, 4096, 4096 * 3, wl.offsets[1] + 64, wl.d]
     for j0, j1 in zip(edges[:-1], edges[1:]):
@@ -676,3 +676,184 @@ def test_stats_momentum_variance_exact(oracle):
             mean = sum(vals) / W
             best = max(best, sum((v - mean) ** 2 for v in vals) / W)
         assert dbg["mvar_max"][T] == float(best)
+
+
+# ----------------------------------- max-norm stochastic baseline (Q-inf) --
+# The pages name this quantiser as the baseline Eq. (1) replaces but do not
+# print it; the reading pinned here is Eq. (1) with max |x| in place of the
+# mean and stochastic rounding, u drawn by SplitMix64 keyed per element.
+
+def test_splitmix64_published_outputs(oracle):
+    """SplitMix64 (Steele, Lea, Flood 2014; Vigna's reference C version):
+    the published first outputs for seeds 1234567 and 0."""
+    want = [6457827717110365317, 3203168211198807973, 9817491932198370423,
+            4593380528125082431, 16408922859458223821]
+    assert [oracle.splitmix64(1234567, k) for k in range(5)] == want
+    assert oracle.splitmix64(0, 0) == 0xE220A8397B1DCDAF
+
+
+def test_minf_is_numpy_max_abs(oracle):
+    rs = np.random.default_rng(21)
+    for n in (1, 7, 4096, 100003):
+        x = (rs.standard_t(2.5, n) * 1e-3).astype(np.float32)
+        x[rs.integers(0, n, max(1, n // 50))] = 0
+        assert oracle.minf(x) == float(np.max(np.abs(x)))
+    x = np.array([0.0, -3.5, 2.0, np.float32(1e-45)], dtype=np.float32)
+    assert oracle.minf(x) == 3.5
+    assert oracle.minf(np.zeros(5, np.float32)) == 0.0
+
+
+def _exact_minf(qmax, e=10):
+    """A max |x| with qmax / max|x| = 2^e exactly."""
+    return float(Fraction(qmax, 2**e))
+
+
+@pytest.mark.parametrize("n", [2, 4, 8])
+def test_qinf_integer_points_ignore_the_draw(oracle, n):
+    """y = qmax * x / max|x| an integer: the code is y whatever the draw."""
+    qmax = 2 ** (n - 1) - 1
+    M = _exact_minf(qmax)
+    for k in range(-qmax, qmax + 1):
+        c = float(Fraction(k, 2**10))
+        for draw in (0, 1 << 63, 2**64 - 1):
+            assert oracle.qinf(c, M, n, draw) == k
+    assert oracle.qinf(0.25, 0.0, n, 2**64 - 1) == 0      # all-zero row
+
+
+def test_qinf_clamps_the_row_maximum(oracle):
+    """x = +-max|x| where the fp64 product qmax/M * M rounds above qmax
+    (M = float32(0.0066045928), y = 7 + 2^-50): a draw of 0 would round up to
+    8, the clamp keeps +-qmax."""
+    M = float(np.float32(0.006604592781513929))
+    assert M * (7.0 / M) > 7.0
+    for draw in (0, 2**64 - 1):
+        assert oracle.qinf(M, M, 4, draw) == 7
+        assert oracle.qinf(-M, M, 4, draw) == -7
+
+
+def test_qinf_draw_threshold_direction(oracle):
+    """y = 2.25: the code is 3 exactly when u = (draw >> 11) / 2^53 < 0.25
+    (probability 0.25 of rounding up), else 2; negatives round toward
+    floor(y) + 1 the same way."""
+    M = _exact_minf(7)
+    c = float(Fraction(9, 4 * 2**10))                        # y = 2.25
+    at = (1 << 51) << 11                                     # u = 0.25
+    below = ((1 << 51) - 1) << 11                            # u = 0.25 - 2^-53
+    assert oracle.qinf(c, M, 4, below) == 3
+    assert oracle.qinf(c, M, 4, at) == 2
+    assert oracle.qinf(c, M, 4, 0) == 3
+    assert oracle.qinf(c, M, 4, 2**64 - 1) == 2
+    # y = -2.25 = -3 + 0.75: up to -2 when u < 0.75
+    assert oracle.qinf(-c, M, 4, (3 << 51) - 1 << 11) == -2
+    assert oracle.qinf(-c, M, 4, (3 << 51) << 11) == -3
+
+
+def test_qinf_unbiased_over_the_stream(oracle):
+    """Stochastic rounding is unbiased: over many draws of the generator the
+    mean code is y (within 5 standard errors of the Bernoulli mean)."""
+    M = _exact_minf(7)
+    N = 40000
+    for yq in (Fraction(13, 10), Fraction(-5, 8), Fraction(61, 10)):
+        c = np.float32(float(yq / 2**10))
+        y = Fraction(float(c)) * 2**10                       # the exact y
+        qs = np.array([oracle.qinf(float(c), M, 4, oracle.splitmix64(99, k)) for k in range(N)])
+        fl = math.floor(y)
+        assert set(np.unique(qs)) <= {fl, fl + 1}
+        p = float(y - fl)
+        se = math.sqrt(p * (1 - p) / N)
+        assert abs(float(np.mean(qs)) - float(y)) < 5 * se + 1e-12
+
+
+def test_quant_linf_rows_and_counters(oracle):
+    """Standalone codes: per (worker, tensor) max |x| exact; element j of
+    worker i at step t uses draw (t*W + i)*d + j of the seeded stream; the
+    dequantised codes are unbiased for x."""
+    wl = wls.Workload(name="qi", tensors=[("a", 4096 + 64), ("b", 192)], W=3, agg="linf",
+                      qbits=4)
+    rs = np.random.default_rng(8)
+    x = np.zeros((wl.W, wl.ld), np.float32)
+    x[:, : wl.d] = (rs.standard_t(2.5, (wl.W, wl.d)) * 1e-3).astype(np.float32)
+    t = 5
+    codes, mv = oracle.quant_linf(wl, x, t)
+    for i in range(wl.W):
+        for T in range(2):
+            a, b = wl.offsets[T], wl.offsets[T + 1]
+            assert mv[i, T] == float(np.max(np.abs(x[i, a:b])))
+    for i, j in ((0, 0), (2, 4100), (1, wl.d - 1)):
+        T = 0 if j < wl.offsets[1] else 1
+        draw = oracle.splitmix64(wl.sr_seed, (t * wl.W + i) * wl.d + j)
+        assert codes[i, j] == oracle.qinf(float(x[i, j]), mv[i, T], 4, draw)
+    assert np.all(codes[:, wl.d:] == 0)
+    # another step draws a different stream
+    codes2, _ = oracle.quant_linf(wl, x, t + 1)
+    assert not np.array_equal(codes, codes2)
+    # unbiased over steps: mean of dequantised codes tends to x
+    acc = np.zeros((wl.W, wl.d))
+    S = 200
+    for s in range(1, S + 1):
+        cs, mv = oracle.quant_linf(wl, x, s)
+        scale = np.repeat(mv / 7.0, np.diff(wl.offsets), axis=1)
+        acc += cs[:, : wl.d] * scale
+    err = acc / S - x[:, : wl.d]
+    sd = np.repeat(mv / 7.0, np.diff(wl.offsets), axis=1) * 0.5 / math.sqrt(S)
+    assert np.all(np.abs(err) <= 6 * sd + 1e-12)
+
+
+def test_qinf_zeroes_most_heavy_tailed_updates(oracle):
+    """The pages' finding (Lion Cub review, Figure 3 and Figure 4): on
+    heavy-tailed update vectors the max-norm quantiser sends most entries to
+    zero and matches few signs, while Eq. (1) keeps most signs."""
+    rs = np.random.default_rng(5)
+    d = 1 << 18
+    wl = wls.flat("ht", d, W=1, agg="linf", qbits=4)
+    x = np.zeros((1, wl.ld), np.float32)
+    x[0, :d] = (rs.standard_t(2.5, d) * 1e-3).astype(np.float32)
+    ci, _ = oracle.quant_linf(wl, x, 1)
+    c1, _ = oracle.quant_l1(wl.with_(agg="l1"), x)
+    zi, z1 = np.mean(ci[0, :d] == 0), np.mean(c1[0, :d] == 0)
+    mi = np.mean(np.sign(ci[0, :d]) == np.sign(x[0, :d]))
+    m1 = np.mean(np.sign(c1[0, :d]) == np.sign(x[0, :d]))
+    assert zi > 0.5 and z1 < 0.2
+    assert m1 > mi + 0.5
+
+
+def test_linf_step_equals_vote_when_magnitudes_are_equal(oracle):
+    """|c| the same everywhere in a row: every code is +-qmax, the integer
+    sum is qmax*(2*count - W), and with odd W and no zeros the step is the
+    majority-vote step bit for bit."""
+    from synth import gen
+    wl_v = wls.Workload(name="eq", tensors=[("a", 4096 + 128), ("b", 64)], W=5, agg="vote")
+    wl_i = wl_v.with_(agg="linf", qbits=4)
+    rs = np.random.default_rng(3)
+    theta = gen.host_theta(wl_v)
+    m = np.zeros((wl_v.W, wl_v.ld), np.float32)
+    g = np.zeros((wl_v.W, wl_v.ld), np.float32)
+    g[:, : wl_v.d] = np.where(rs.random((wl_v.W, wl_v.d)) < 0.5, -1.0, 1.0) * 2.0**-9
+    tv, mvv = theta.copy(), m.copy()
+    dv = oracle.step(wl_v, tv, mvv, g, 3, debug=True)
+    ti, mii = theta.copy(), m.copy()
+    di = oracle.step(wl_i, ti, mii, g, 3, debug=True)
+    assert np.array_equal(np.abs(di["codes"][:, : wl_v.d]), np.full((wl_v.W, wl_v.d), 7))
+    assert np.array_equal(di["sums"], 7 * (2 * dv["counts"].astype(np.int32) - wl_v.W))
+    assert np.array_equal(di["sign"], dv["sign"])
+    assert np.array_equal(ti, tv) and np.array_equal(mii, mvv)
+    assert di["stats"][:, 0].sum() == 0                      # no vote ties on this path
+
+
+def test_linf_step_codes_are_standalone_codes_of_c(oracle):
+    """Inside the step, worker i's codes are the standalone max-norm codes of
+    its c_i at the same step t (same max |c| per tensor, same draws)."""
+    from synth import gen
+    wl = wls.Workload(name="sc", tensors=[("a", 4096 + 640), ("b", 128)], W=3, agg="linf",
+                      qbits=4, grad_dtype="bf16")
+    theta = gen.host_theta(wl)
+    m = gen.host_m(wl)
+    g = gen.host_g(wl, 4)
+    c = np.zeros((wl.W, wl.ld), np.float32)
+    for i in range(wl.W):
+        c[i, : wl.d] = oracle.c_row(wl, m[i, : wl.d], g[i, : wl.d])
+    want, mv = oracle.quant_linf(wl, c, 4)
+    assert np.array_equal(mv, oracle.minf_all(wl, m, g))
+    got = oracle.step(wl, theta, m.copy(), g, 4, debug=True)
+    assert np.array_equal(got["codes"][:, : wl.d], want[:, : wl.d])
+    assert np.array_equal(got["sums"], want[:, : wl.d].astype(np.int32).sum(axis=0))
