@@ -8,19 +8,19 @@ sign updates the parameters and each worker's momentum.  `_abi` mirrors the C
 entry points; `LionCub` keeps a context and its workspace together.
 """
 from . import _abi
-from ._abi import (AGG_AVG, AGG_L1SUM, AGG_VOTE, BF16, F32, TIE_PARITY, TIE_ZERO, LionCubError,
-                   lioncub_apply, lioncub_destroy, lioncub_init, lioncub_pack,
+from ._abi import (AGG_AVG, AGG_L1SUM, AGG_LINFSUM, AGG_VOTE, BF16, F32, TIE_PARITY, TIE_ZERO,
+                   LionCubError, lioncub_apply, lioncub_destroy, lioncub_init, lioncub_pack,
                    lioncub_pack_codes, lioncub_profile_begin, lioncub_profile_end,
-                   lioncub_quant_l1, lioncub_set_stream, lioncub_step, lioncub_strerror,
+                   lioncub_quant_l1, lioncub_quant_linf, lioncub_set_stream, lioncub_step, lioncub_strerror,
                    lioncub_unpack_sum, lioncub_vote, lioncub_vote_bits, lioncub_workspace_bytes,
                    make_config)
 
 __all__ = ["LionCub", "LionCubError", "make_config", "lioncub_workspace_bytes", "lioncub_init",
            "lioncub_set_stream", "lioncub_step", "lioncub_pack", "lioncub_vote",
-           "lioncub_quant_l1", "lioncub_vote_bits", "lioncub_apply", "lioncub_pack_codes",
-           "lioncub_unpack_sum", "lioncub_profile_begin", "lioncub_profile_end",
+           "lioncub_quant_l1", "lioncub_quant_linf", "lioncub_vote_bits", "lioncub_apply",
+           "lioncub_pack_codes", "lioncub_unpack_sum", "lioncub_profile_begin", "lioncub_profile_end",
            "lioncub_destroy", "lioncub_strerror", "F32", "BF16", "AGG_VOTE", "AGG_L1SUM",
-           "AGG_AVG", "TIE_PARITY", "TIE_ZERO"]
+           "AGG_AVG", "AGG_LINFSUM", "TIE_PARITY", "TIE_ZERO"]
 
 
 class LionCub:
@@ -31,17 +31,20 @@ class LionCub:
 
     def __init__(self, d, W, tensor_offsets=None, ld=None, sync_m=None, sync_every=1,
                  theta_dtype="f32", grad_dtype="f32", agg="vote", qbits=0, tie="parity",
-                 beta1=0.9, beta2=0.99, lr=1e-4, wd=0.1, device="cuda", stream=None):
+                 beta1=0.9, beta2=0.99, lr=1e-4, wd=0.1, sr_seed=0, device="cuda", stream=None):
         import torch
+        aggs = {"vote": AGG_VOTE, "l1": AGG_L1SUM, "avg": AGG_AVG, "linf": AGG_LINFSUM}
+        if agg not in aggs:
+            raise ValueError(f"agg must be one of {sorted(aggs)}, got {agg!r}")
         ld = ld if ld is not None else (d + 63) // 64 * 64
         offs = tensor_offsets if tensor_offsets is not None else [0, d]
         self.cfg = make_config(
             d, ld, W, offs, sync_m=sync_m, sync_every=sync_every,
             theta_dtype=BF16 if theta_dtype == "bf16" else F32,
             grad_dtype=BF16 if grad_dtype == "bf16" else F32,
-            agg={"l1": AGG_L1SUM, "avg": AGG_AVG}.get(agg, AGG_VOTE), qbits=qbits,
+            agg=aggs[agg], qbits=qbits,
             tie_mode=TIE_ZERO if tie == "zero" else TIE_PARITY,
-            beta1=beta1, beta2=beta2, lr=lr, wd=wd)
+            beta1=beta1, beta2=beta2, lr=lr, wd=wd, sr_seed=sr_seed)
         self.d, self.ld, self.W, self.n_tensors = d, ld, W, len(offs) - 1
         nbytes = lioncub_workspace_bytes(self.cfg)
         if nbytes == 0:
@@ -61,6 +64,9 @@ class LionCub:
 
     def quant_l1(self, x, codes, m1=None):
         lioncub_quant_l1(self.ctx, x, codes, m1)
+
+    def quant_linf(self, x, t, codes, minf=None):
+        lioncub_quant_linf(self.ctx, x, t, codes, minf)
 
     def vote_bits(self, bits, t, sign_bits, zero_bits=None):
         lioncub_vote_bits(self.ctx, bits, t, sign_bits, zero_bits)

@@ -14,15 +14,18 @@ LIB_PATH = os.path.join(HERE, "liblioncub.so")
 
 OK, EINVAL, EALIGN, EWORKSPACE, EDEVICE, EUNSUPPORTED = 0, -1, -2, -3, -4, -5
 F32, BF16 = 0, 1
-AGG_VOTE, AGG_L1SUM, AGG_AVG = 0, 1, 2
+AGG_VOTE, AGG_L1SUM, AGG_AVG, AGG_LINFSUM = 0, 1, 2, 3
 TIE_PARITY, TIE_ZERO = 0, 1
 (K_VOTE_STEP, K_M1_PARTIAL, K_M1_FINALIZE, K_L1_STEP, K_PACK, K_VOTE, K_QUANT, K_VOTE_BITS,
- K_APPLY, K_PACK_CODES, K_UNPACK_SUM, K_AVG_STEP, K_STATS, K_COUNT) = range(14)
+ K_APPLY, K_PACK_CODES, K_UNPACK_SUM, K_AVG_STEP, K_STATS, K_LINF_STEP, K_QUANT_LINF,
+ K_COUNT) = range(16)
 KERNEL_NAMES = ["vote_step", "m1_partial", "m1_finalize", "l1_step", "pack", "vote", "quant",
-                "vote_bits", "apply", "pack_codes", "unpack_sum", "avg_step", "stats"]
+                "vote_bits", "apply", "pack_codes", "unpack_sum", "avg_step", "stats",
+                "linf_step", "quant_linf"]
 
 EXPORTS = ["lioncub_workspace_bytes", "lioncub_init", "lioncub_set_stream", "lioncub_step",
-           "lioncub_pack", "lioncub_vote", "lioncub_quant_l1", "lioncub_vote_bits",
+           "lioncub_pack", "lioncub_vote", "lioncub_quant_l1", "lioncub_quant_linf",
+           "lioncub_vote_bits",
            "lioncub_apply", "lioncub_pack_codes", "lioncub_unpack_sum", "lioncub_profile_begin",
            "lioncub_profile_end", "lioncub_destroy", "lioncub_strerror"]
 
@@ -34,6 +37,7 @@ class lioncub_config(C.Structure):
         ("sync_every", C.c_int32), ("theta_dtype", C.c_int32), ("grad_dtype", C.c_int32),
         ("agg", C.c_int32), ("qbits", C.c_int32), ("tie_mode", C.c_int32),
         ("beta1", C.c_float), ("beta2", C.c_float), ("lr", C.c_float), ("wd", C.c_float),
+        ("sr_seed", C.c_uint64),
     ]
 
 
@@ -69,6 +73,8 @@ def lib():
         L.lioncub_vote.restype = C.c_int
         L.lioncub_quant_l1.argtypes = [vp, vp, vp, vp]
         L.lioncub_quant_l1.restype = C.c_int
+        L.lioncub_quant_linf.argtypes = [vp, vp, C.c_int64, vp, vp]
+        L.lioncub_quant_linf.restype = C.c_int
         L.lioncub_vote_bits.argtypes = [vp, vp, i64, vp, vp]
         L.lioncub_vote_bits.restype = C.c_int
         L.lioncub_apply.argtypes = [vp, vp, vp, vp, i64, vp, vp]
@@ -113,7 +119,7 @@ def _stream_handle(stream=None):
 
 def make_config(d, ld, W, tensor_offsets, sync_m=None, sync_every=1, theta_dtype=F32,
                 grad_dtype=F32, agg=AGG_VOTE, qbits=0, tie_mode=TIE_PARITY, beta1=0.9,
-                beta2=0.99, lr=1e-4, wd=0.1):
+                beta2=0.99, lr=1e-4, wd=0.1, sr_seed=0):
     """A lioncub_config plus the host arrays it points to (kept alive on it)."""
     cfg = lioncub_config()
     offs = (C.c_int64 * len(tensor_offsets))(*[int(v) for v in tensor_offsets])
@@ -127,6 +133,7 @@ def make_config(d, ld, W, tensor_offsets, sync_m=None, sync_every=1, theta_dtype
     cfg.sync_every, cfg.theta_dtype, cfg.grad_dtype = sync_every, theta_dtype, grad_dtype
     cfg.agg, cfg.qbits, cfg.tie_mode = agg, qbits, tie_mode
     cfg.beta1, cfg.beta2, cfg.lr, cfg.wd = beta1, beta2, lr, wd
+    cfg.sr_seed = int(sr_seed) & (2**64 - 1)
     return cfg
 
 
@@ -168,6 +175,11 @@ def lioncub_vote(ctx, bits, t, counts=None, sign=None):
 
 def lioncub_quant_l1(ctx, x, codes, m1=None):
     _check("lioncub_quant_l1", lib().lioncub_quant_l1(ctx, _ptr(x), _ptr(codes), _ptr(m1)))
+
+
+def lioncub_quant_linf(ctx, x, t, codes, minf=None):
+    _check("lioncub_quant_linf",
+           lib().lioncub_quant_linf(ctx, _ptr(x), int(t), _ptr(codes), _ptr(minf)))
 
 
 def lioncub_vote_bits(ctx, bits, t, sign_bits, zero_bits=None):

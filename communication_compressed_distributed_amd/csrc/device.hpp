@@ -213,4 +213,24 @@ __device__ __forceinline__ uint32_t sign_bit(float c, uint32_t parity) {
   return c > 0.0f ? 1u : (c < 0.0f ? 0u : parity);
 }
 
+// SplitMix64 output function (the finaliser of Steele, Lea and Flood's
+// generator; see kGamma for the counter that feeds it).
+__device__ __forceinline__ uint64_t mix64(uint64_t z) {
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+// Stochastic rounding of y = c * scale (fp64) onto the integers: floor(y) + 1
+// when u < y - floor(y), u = (draw >> 11) * 2^-53 uniform in [0, 1), else
+// floor(y); then clamped to +-qmax.  Every step is exact except the product.
+__device__ __forceinline__ int sr_code(float c, double scale, double qmax, uint64_t draw) {
+  const double y = static_cast<double>(c) * scale;
+  const double fl = __builtin_floor(y);
+  const double u = static_cast<double>(draw >> 11) * 0x1.0p-53;
+  double q = fl + (u < (y - fl) ? 1.0 : 0.0);
+  q = fmin(fmax(q, -qmax), qmax);
+  return static_cast<int>(q);
+}
+
 }  // namespace lioncub

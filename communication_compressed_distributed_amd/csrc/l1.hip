@@ -1,4 +1,5 @@
-// l1.hip -- mean |c| (the M1 of Eq. (1)) and standalone L1 codes, gfx950.
+// l1.hip -- mean |c| (the M1 of Eq. (1)) or max |c| (the max-norm
+// baseline), and standalone codes of both quantisers, gfx950.
 //
 // Eq. (1) of the Lion Cub page (pith.science review, "What carries the
 // argument"): Q1(x) = clamp(round((2^(n-1)-1) x / M1(x)), 2^(n-1)-1), M1 the
@@ -17,6 +18,11 @@
 // way (partial l in lane l), then one wave gives lane l the group values l,
 // l+64, ... in order, folds, and divides by the element count.  Only magnitudes are added, so
 // the partials are non-negative and independent of sign.
+//
+// The max-norm baseline (MX = true) runs the same tree with max in place of
+// the sum and no division: a maximum is exact in any order.  Its codes round
+// stochastically (sr_code), with the SplitMix64 draw of element j of worker
+// i at step t taken at counter (t*W + i)*d + j.
 #include "device.hpp"
 #include "layout.hpp"
 
@@ -24,15 +30,23 @@
 
 namespace lioncub {
 
+// The tree's combining step: a sum, or for the max-norm a maximum.
+template <bool MX>
+__device__ __forceinline__ double red(double a, double b) {
+  if constexpr (MX) return fmax(a, b);
+  else return a + b;
+}
+
+template <bool MX = false>
 __device__ __forceinline__ double wave_fold(double v) {
 #pragma unroll
-  for (int s = 32; s >= 1; s >>= 1) v = v + __shfl_xor(v, s, kWave);
+  for (int s = 32; s >= 1; s >>= 1) v = red<MX>(v, __shfl_xor(v, s, kWave));
   return v;
 }
 
 // Lane sum of one worker over the block: acc = sum over the 4 rounds of
 // ((e0+e1)+(e2+e3)), e = |c| in fp64 (zero past the end of the tensor).
-template <int SRC, int GT>
+template <int SRC, int GT, bool MX>
 __device__ __forceinline__ double lane_sum(const M1Params& p, const F4 (&a)[kRounds],
                                            const F4 (&b)[kRounds]) {
   double acc = 0.0;
@@ -46,7 +60,7 @@ __device__ __forceinline__ double lane_sum(const M1Params& p, const F4 (&a)[kRou
       else c = (p.beta1 * a[r].v[k]) + (p.omega1 * b[r].v[k]);
       e[k] = fabs(static_cast<double>(c));
     }
-    acc = acc + ((e[0] + e[1]) + (e[2] + e[3]));
+    acc = red<MX>(acc, red<MX>(red<MX>(e[0], e[1]), red<MX>(e[2], e[3])));
   }
   return acc;
 }
@@ -95,7 +109,7 @@ __device__ __forceinline__ void m1_load(const M1Params& p, const BlockEnt& be, i
 // addition commutes).  After log2(NW) such steps each lane holds one worker;
 // the remaining distances fold it like wave_fold.  17 shuffles instead of 96
 // for 16 workers.  Returns the total of worker wk(lane) in `out`.
-template <int NW>
+template <int NW, bool MX>
 __device__ __forceinline__ double fold_many(double (&v)[NW], int* wk) {
   const int lane = threadIdx.x & 63;
   int base = 0;
@@ -111,14 +125,14 @@ __device__ __forceinline__ double fold_many(double (&v)[NW], int* wk) {
       const double send = upper ? v[k] : v[k + h];
       const double keep = upper ? v[k + h] : v[k];
       const double recv = __shfl_xor(send, s, kWave);
-      v[k] = keep + recv;
+      v[k] = red<MX>(keep, recv);
     }
     if (upper) base += h;
     n = h;
     s >>= 1;
   }
   double r = v[0];
-  for (; s >= 1; s >>= 1) r = r + __shfl_xor(r, s, kWave);
+  for (; s >= 1; s >>= 1) r = red<MX>(r, __shfl_xor(r, s, kWave));
   *wk = base;
   return r;
 }
@@ -129,7 +143,7 @@ __device__ __forceinline__ double fold_many(double (&v)[NW], int* wk) {
 // vector loads with no per-lane predicates; the ragged last block of a
 // tensor takes the masked path.  With WT = 4, 8 or 16 workers the lane sums
 // stay in registers and are folded together at the end (fold_many).
-template <int SRC, int GT, bool FULL, int WT>
+template <int SRC, int GT, bool FULL, int WT, bool MX>
 __device__ __forceinline__ void m1_block(const M1Params& p, const BlockEnt& be,
                                          double (*sh_w)[256]) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -148,10 +162,10 @@ __device__ __forceinline__ void m1_block(const M1Params& p, const BlockEnt& be,
       F4 a[WB][kRounds], b[WB][kRounds];
       m1_load<SRC, GT, FULL, WB>(p, be, i0, W, nv, a, b);
 #pragma unroll
-      for (int u = 0; u < WB; ++u) acc[i0 + u] = lane_sum<SRC, GT>(p, a[u], b[u]);
+      for (int u = 0; u < WB; ++u) acc[i0 + u] = lane_sum<SRC, GT, MX>(p, a[u], b[u]);
     }
     int wk = 0;
-    const double tot = fold_many<WT>(acc, &wk);
+    const double tot = fold_many<WT, MX>(acc, &wk);
     if ((lane & (64 / WT - 1)) == 0) sh_w[wave][wk] = tot;
   } else {
     // generic W or a ragged block: one worker at a time, folded at once
@@ -159,22 +173,22 @@ __device__ __forceinline__ void m1_block(const M1Params& p, const BlockEnt& be,
     for (int i = 0; i < W; ++i) {
       F4 a[1][kRounds], b[1][kRounds];
       m1_load<SRC, GT, FULL, 1>(p, be, i, W, nv, a, b);
-      const double tot = wave_fold(lane_sum<SRC, GT>(p, a[0], b[0]));
+      const double tot = wave_fold<MX>(lane_sum<SRC, GT, MX>(p, a[0], b[0]));
       if (lane == 0) sh_w[wave][i] = tot;
     }
   }
 }
 
-template <int SRC, int GT, int WT>
+template <int SRC, int GT, int WT, bool MX>
 __global__ __launch_bounds__(kThreads) void k_m1_partial(M1Params p) {
   __shared__ double sh_w[4][256];  // [wave][worker]
   const BlockEnt be = block_of(p.blk, p.flat, p.d);
   const int tid = threadIdx.x;
-  if (be.len == kBlock) m1_block<SRC, GT, true, WT>(p, be, sh_w);
-  else m1_block<SRC, GT, false, 0>(p, be, sh_w);
+  if (be.len == kBlock) m1_block<SRC, GT, true, WT, MX>(p, be, sh_w);
+  else m1_block<SRC, GT, false, 0, MX>(p, be, sh_w);
   __syncthreads();
   for (int i = tid; i < p.W; i += kThreads) {
-    const double P = (sh_w[0][i] + sh_w[1][i]) + (sh_w[2][i] + sh_w[3][i]);
+    const double P = red<MX>(red<MX>(sh_w[0][i], sh_w[1][i]), red<MX>(sh_w[2][i], sh_w[3][i]));
     p.partial[static_cast<int64_t>(blockIdx.x) * p.W + i] = P;  // one run per block
   }
 }
@@ -182,6 +196,7 @@ __global__ __launch_bounds__(kThreads) void k_m1_partial(M1Params p) {
 // Group values: one workgroup per (worker, group of 256 consecutive block
 // partials of one tensor); lane l takes partial l (0.0 past the tensor's last
 // block), each wave folds, then (w0+w1)+(w2+w3).
+template <bool MX>
 __global__ __launch_bounds__(kThreads) void k_m1_group(M1Params p) {
   __shared__ double sh[4];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -189,15 +204,17 @@ __global__ __launch_bounds__(kThreads) void k_m1_group(M1Params p) {
   const int i = static_cast<int>(gid / p.ngrp), gg = static_cast<int>(gid % p.ngrp);
   const GroupEnt ge = p.grp[gg];
   double v = tid < ge.cnt ? p.partial[static_cast<int64_t>(ge.blk + tid) * p.W + i] : 0.0;
-  v = wave_fold(v);
+  v = wave_fold<MX>(v);
   if (lane == 0) sh[wave] = v;
   __syncthreads();
-  if (tid == 0) p.gval[static_cast<int64_t>(i) * p.ngrp + gg] = (sh[0] + sh[1]) + (sh[2] + sh[3]);
+  if (tid == 0)
+    p.gval[static_cast<int64_t>(i) * p.ngrp + gg] = red<MX>(red<MX>(sh[0], sh[1]), red<MX>(sh[2], sh[3]));
 }
 
 // One wave per (worker, tensor): lane l sums group values l, l+64, ... in
 // order, the wave folds, M1 = total / n, scale = Qmax / M1 (0 when M1 == 0,
-// which makes every code 0).
+// which makes every code 0).  Max-norm: the maximum, not divided.
+template <bool MX>
 __global__ __launch_bounds__(kThreads) void k_m1_finalize(M1Params p) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t pair = static_cast<int64_t>(blockIdx.x) * 4 + wave;
@@ -206,17 +223,19 @@ __global__ __launch_bounds__(kThreads) void k_m1_finalize(M1Params p) {
   const TensorEnt te = p.tens[T];
   const double* G = p.gval + static_cast<int64_t>(i) * p.ngrp + te.grp0;
   double acc = 0.0;
-  for (int k = lane; k < te.ngrp; k += kWave) acc = acc + G[k];
-  acc = wave_fold(acc);
+  for (int k = lane; k < te.ngrp; k += kWave) acc = red<MX>(acc, G[k]);
+  acc = wave_fold<MX>(acc);
   if (lane == 0) {
-    const double M = acc / static_cast<double>(te.n);
+    const double M = MX ? acc : acc / static_cast<double>(te.n);
     p.m1[pair] = M;
     if (p.m1_out) p.m1_out[pair] = M;
     if (p.qmax > 0) p.scale[pair] = M == 0.0 ? 0.0 : static_cast<double>(p.qmax) / M;
   }
 }
 
-// Eq. (1) codes of x: one workgroup per block, all workers.
+// Eq. (1) codes of x (or, MX, the stochastic max-norm codes): one
+// workgroup per block, all workers.
+template <bool MX>
 __global__ __launch_bounds__(kThreads) void k_quant_codes(M1Params p, int8_t* __restrict__ codes) {
   const BlockEnt be = block_of(p.blk, p.flat, p.d);
   const int tid = threadIdx.x;
@@ -232,48 +251,68 @@ __global__ __launch_bounds__(kThreads) void k_quant_codes(M1Params p, int8_t* __
       const int64_t idx = static_cast<int64_t>(i) * p.ld + be.start + loc;
       const F4 x = ldnt_f32x4(p.x + idx, nv);
       uint32_t packed = 0;
+      // counter of element k: (t*W + i)*d + j, j = be.start + loc + k
+      const uint64_t z0 = p.seed + (static_cast<uint64_t>(
+          (static_cast<uint64_t>(p.t) * static_cast<uint64_t>(p.W) + static_cast<uint64_t>(i)) *
+              static_cast<uint64_t>(p.d) + static_cast<uint64_t>(be.start + loc)) + 1u) * kGamma;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        double y = __builtin_rint(static_cast<double>(x.v[k]) * s);
-        y = fmin(fmax(y, -qm), qm);
-        packed |= (static_cast<uint32_t>(static_cast<int>(y)) & 0xFFu) << (8 * k);
+        int qc;
+        if constexpr (MX) {
+          qc = sr_code(x.v[k], s, qm, mix64(z0 + static_cast<uint64_t>(k) * kGamma));
+        } else {
+          double y = __builtin_rint(static_cast<double>(x.v[k]) * s);
+          y = fmin(fmax(y, -qm), qm);
+          qc = static_cast<int>(y);
+        }
+        packed |= (static_cast<uint32_t>(qc) & 0xFFu) << (8 * k);
       }
       st_b4(codes + idx, packed, nv);
     }
   }
 }
 
-template <int SRC, int GT>
+template <int SRC, int GT, bool MX>
 static void launch_m1_t(const M1Params& p, hipStream_t st) {
   const dim3 g(p.nblk), b(kThreads);
   switch (p.W) {
-    case 4: hipLaunchKernelGGL((k_m1_partial<SRC, GT, 4>), g, b, 0, st, p); break;
-    case 8: hipLaunchKernelGGL((k_m1_partial<SRC, GT, 8>), g, b, 0, st, p); break;
-    case 16: hipLaunchKernelGGL((k_m1_partial<SRC, GT, 16>), g, b, 0, st, p); break;
-    default: hipLaunchKernelGGL((k_m1_partial<SRC, GT, 0>), g, b, 0, st, p); break;
+    case 4: hipLaunchKernelGGL((k_m1_partial<SRC, GT, 4, MX>), g, b, 0, st, p); break;
+    case 8: hipLaunchKernelGGL((k_m1_partial<SRC, GT, 8, MX>), g, b, 0, st, p); break;
+    case 16: hipLaunchKernelGGL((k_m1_partial<SRC, GT, 16, MX>), g, b, 0, st, p); break;
+    default: hipLaunchKernelGGL((k_m1_partial<SRC, GT, 0, MX>), g, b, 0, st, p); break;
   }
 }
 
-hipError_t launch_m1(const M1Params& p, int src_x, int grad_bf16, hipStream_t st) {
-  if (src_x) launch_m1_t<0, 0>(p, st);
-  else if (grad_bf16) launch_m1_t<1, 1>(p, st);
-  else launch_m1_t<1, 0>(p, st);
+template <bool MX>
+static void launch_m1_m(const M1Params& p, int src_x, int grad_bf16, hipStream_t st) {
+  if (src_x) launch_m1_t<0, 0, MX>(p, st);
+  else if (grad_bf16) launch_m1_t<1, 1, MX>(p, st);
+  else launch_m1_t<1, 0, MX>(p, st);
+}
+
+hipError_t launch_m1(const M1Params& p, int src_x, int grad_bf16, int maxnorm, hipStream_t st) {
+  if (maxnorm) launch_m1_m<true>(p, src_x, grad_bf16, st);
+  else launch_m1_m<false>(p, src_x, grad_bf16, st);
   return hipGetLastError();
 }
 
-hipError_t launch_m1_finalize(const M1Params& p, hipStream_t st) {
+hipError_t launch_m1_finalize(const M1Params& p, int maxnorm, hipStream_t st) {
   const int64_t groups = static_cast<int64_t>(p.W) * p.ngrp;
-  hipLaunchKernelGGL(k_m1_group, dim3(static_cast<unsigned>(groups)), dim3(kThreads), 0, st, p);
+  const dim3 gg(static_cast<unsigned>(groups)), b(kThreads);
+  if (maxnorm) hipLaunchKernelGGL(k_m1_group<true>, gg, b, 0, st, p);
+  else hipLaunchKernelGGL(k_m1_group<false>, gg, b, 0, st, p);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t pairs = static_cast<int64_t>(p.W) * p.nT;
-  hipLaunchKernelGGL(k_m1_finalize, dim3(static_cast<unsigned>((pairs + 3) / 4)), dim3(kThreads),
-                     0, st, p);
+  const dim3 gf(static_cast<unsigned>((pairs + 3) / 4));
+  if (maxnorm) hipLaunchKernelGGL(k_m1_finalize<true>, gf, b, 0, st, p);
+  else hipLaunchKernelGGL(k_m1_finalize<false>, gf, b, 0, st, p);
   return hipGetLastError();
 }
 
-hipError_t launch_quant_codes(const M1Params& p, int8_t* codes, hipStream_t st) {
-  hipLaunchKernelGGL(k_quant_codes, dim3(p.nblk), dim3(kThreads), 0, st, p, codes);
+hipError_t launch_quant_codes(const M1Params& p, int8_t* codes, int maxnorm, hipStream_t st) {
+  if (maxnorm) hipLaunchKernelGGL(k_quant_codes<true>, dim3(p.nblk), dim3(kThreads), 0, st, p, codes);
+  else hipLaunchKernelGGL(k_quant_codes<false>, dim3(p.nblk), dim3(kThreads), 0, st, p, codes);
   return hipGetLastError();
 }
 

@@ -47,7 +47,8 @@ struct StepParams {
   void* theta;         // [d] fp32 or bf16
   float* m;            // [W][ld]
   const void* g;       // [W][ld] fp32 or bf16
-  const double* scale; // [W][nT] (L1 path): Qmax / M1, 0 when M1 == 0
+  const double* scale; // [W][nT] (quantised paths): Qmax / M1 or Qmax / max|c|,
+                       // 0 when that norm is 0
   int64_t ld;
   int32_t W;
   int32_t nT;
@@ -59,6 +60,10 @@ struct StepParams {
   int32_t flat;        // one tensor: block b starts at b*kBlock (no table load)
   int32_t any_sync;    // some tensor is averaged (else no tensor-table load)
   int64_t d;
+  // stochastic rounding (max-norm path): draw of element j of worker i is
+  // output (t*W + i)*d + j of the SplitMix64 stream keyed by seed
+  uint64_t seed;
+  int64_t t;
   // global sign given as bit planes (apply mode): [ld/64] each, zero may be null
   const uint64_t* sign_bits;
   const uint64_t* zero_bits;
@@ -97,10 +102,17 @@ struct M1Params {
   int32_t flat;        // one tensor: block b starts at b*kBlock (no table load)
   int64_t d;
   float beta1, omega1;
+  uint64_t seed;       // max-norm codes: stochastic-rounding key and step
+  int64_t t;
 };
 
 // Aggregation modes of the fused step kernel.
-enum Agg : int { kAggVote = 0, kAggL1 = 1, kAggAvg = 2, kAggApply = 3 };
+enum Agg : int { kAggVote = 0, kAggL1 = 1, kAggAvg = 2, kAggApply = 3, kAggLinf = 4 };
+
+// SplitMix64 (Steele, Lea and Flood, "Fast splittable pseudorandom number
+// generators", OOPSLA 2014) as a counter-based generator: output k of the
+// stream keyed by s is mix(s + (k+1)*gamma).
+constexpr uint64_t kGamma = 0x9E3779B97F4A7C15ull;
 
 // Block b's descriptor; a single-tensor vector needs no table load.
 __device__ __forceinline__ BlockEnt block_of(const BlockEnt* blk, int flat, int64_t d) {

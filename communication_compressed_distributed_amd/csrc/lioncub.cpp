@@ -19,9 +19,9 @@ hipError_t launch_step(const StepParams& p, int nblk, int theta_bf16, int grad_b
 hipError_t launch_zero_tail_words(uint64_t* bits, int64_t words, int64_t first, int W,
                                   hipStream_t st);
 hipError_t launch_stats_reduce(const StepParams& p, int nT, hipStream_t st);
-hipError_t launch_m1(const M1Params& p, int src_x, int grad_bf16, hipStream_t st);
-hipError_t launch_m1_finalize(const M1Params& p, hipStream_t st);
-hipError_t launch_quant_codes(const M1Params& p, int8_t* codes, hipStream_t st);
+hipError_t launch_m1(const M1Params& p, int src_x, int grad_bf16, int maxnorm, hipStream_t st);
+hipError_t launch_m1_finalize(const M1Params& p, int maxnorm, hipStream_t st);
+hipError_t launch_quant_codes(const M1Params& p, int8_t* codes, int maxnorm, hipStream_t st);
 hipError_t launch_pack(const float* x, uint64_t* bits, int64_t d, int64_t ld, int W,
                        uint32_t parity, hipStream_t st);
 hipError_t launch_vote(const uint64_t* bits, uint8_t* counts, int8_t* sign, int64_t d, int64_t ld,
@@ -83,9 +83,12 @@ int check_config(const lioncub_config* c, int64_t* nblk, int64_t* ngrp) {
   if ((c->theta_dtype != LIONCUB_F32 && c->theta_dtype != LIONCUB_BF16) ||
       (c->grad_dtype != LIONCUB_F32 && c->grad_dtype != LIONCUB_BF16))
     return LIONCUB_EINVAL;
-  if (c->agg != LIONCUB_AGG_VOTE && c->agg != LIONCUB_AGG_L1SUM && c->agg != LIONCUB_AGG_AVG)
+  if (c->agg != LIONCUB_AGG_VOTE && c->agg != LIONCUB_AGG_L1SUM && c->agg != LIONCUB_AGG_AVG &&
+      c->agg != LIONCUB_AGG_LINFSUM)
     return LIONCUB_EINVAL;
-  if (c->agg == LIONCUB_AGG_L1SUM && (c->qbits < 2 || c->qbits > 8)) return LIONCUB_EINVAL;
+  if ((c->agg == LIONCUB_AGG_L1SUM || c->agg == LIONCUB_AGG_LINFSUM) &&
+      (c->qbits < 2 || c->qbits > 8))
+    return LIONCUB_EINVAL;
   if (c->tie_mode != LIONCUB_TIE_PARITY && c->tie_mode != LIONCUB_TIE_ZERO) return LIONCUB_EINVAL;
   if (!finite(c->beta1) || !finite(c->beta2) || !finite(c->lr) || !finite(c->wd))
     return LIONCUB_EINVAL;
@@ -170,6 +173,7 @@ void fill_step_params(const lioncub_ctx* c, StepParams* p) {
   p->any_sync = c->any_sync;
   p->d = c->cfg.d;
   p->qmax = c->cfg.qbits >= 2 ? (1 << (c->cfg.qbits - 1)) - 1 : 0;
+  p->seed = c->cfg.sr_seed;
 }
 
 void fill_m1_params(const lioncub_ctx* c, M1Params* p) {
@@ -191,6 +195,7 @@ void fill_m1_params(const lioncub_ctx* c, M1Params* p) {
   p->omega1 = 1.0f - c->cfg.beta1;
   p->flat = c->cfg.n_tensors == 1;
   p->d = c->cfg.d;
+  p->seed = c->cfg.sr_seed;
 }
 
 int dev_status(hipError_t e) { return e == hipSuccess ? LIONCUB_OK : LIONCUB_EDEVICE; }
@@ -293,7 +298,8 @@ int lioncub_step(lioncub_ctx* ctx, void* theta, float* m, const void* g, int64_t
   if (!ctx || !theta || !m || !g || t < 1) return LIONCUB_EINVAL;
   if (!aligned(theta, 16) || !aligned(m, 16) || !aligned(g, 16)) return LIONCUB_EALIGN;
   const lioncub_config& cf = ctx->cfg;
-  const bool l1 = cf.agg == LIONCUB_AGG_L1SUM;
+  const bool linf = cf.agg == LIONCUB_AGG_LINFSUM;
+  const bool l1 = cf.agg == LIONCUB_AGG_L1SUM || linf;  // the quantised paths
   StepParams p;
   fill_step_params(ctx, &p);
   p.theta = theta;
@@ -301,8 +307,11 @@ int lioncub_step(lioncub_ctx* ctx, void* theta, float* m, const void* g, int64_t
   p.g = g;
   p.parity = static_cast<int32_t>(t & 1);
   p.avg_step = (t % cf.sync_every) == 0;
-  const int kind = l1 ? LIONCUB_K_L1_STEP
-                     : (cf.agg == LIONCUB_AGG_AVG ? LIONCUB_K_AVG_STEP : LIONCUB_K_VOTE_STEP);
+  p.t = t;
+  const int kind = linf ? LIONCUB_K_LINF_STEP
+                 : l1   ? LIONCUB_K_L1_STEP
+                 : (cf.agg == LIONCUB_AGG_AVG ? LIONCUB_K_AVG_STEP : LIONCUB_K_VOTE_STEP);
+  const int agg = linf ? kAggLinf : cf.agg;
   if (dbg) {
     if ((dbg->bits || dbg->counts) && l1) return LIONCUB_EINVAL;
     if ((dbg->codes || dbg->sums || dbg->m1) && !l1) return LIONCUB_EINVAL;
@@ -325,13 +334,14 @@ int lioncub_step(lioncub_ctx* ctx, void* theta, float* m, const void* g, int64_t
     q.m = m;
     q.g = g;
     q.m1_out = dbg ? dbg->m1 : nullptr;
-    e = run(ctx, LIONCUB_K_M1_PARTIAL, [&] { return launch_m1(q, 0, cf.grad_dtype, ctx->stream); });
+    e = run(ctx, LIONCUB_K_M1_PARTIAL,
+            [&] { return launch_m1(q, 0, cf.grad_dtype, linf, ctx->stream); });
     if (e == hipSuccess)
-      e = run(ctx, LIONCUB_K_M1_FINALIZE, [&] { return launch_m1_finalize(q, ctx->stream); });
+      e = run(ctx, LIONCUB_K_M1_FINALIZE, [&] { return launch_m1_finalize(q, linf, ctx->stream); });
   }
   if (e == hipSuccess)
     e = run(ctx, kind, [&] {
-      return launch_step(p, ctx->nblk, cf.theta_dtype, cf.grad_dtype, cf.agg, ctx->stream);
+      return launch_step(p, ctx->nblk, cf.theta_dtype, cf.grad_dtype, agg, ctx->stream);
     });
   if (e == hipSuccess && p.bits)
     e = launch_zero_tail_words(p.bits, cf.ld / 64, (cf.d + 63) / 64, cf.W, ctx->stream);
@@ -422,11 +432,30 @@ int lioncub_quant_l1(lioncub_ctx* ctx, const float* x, int8_t* codes, double* m1
   fill_m1_params(ctx, &q);
   q.x = x;
   q.m1_out = m1;
-  hipError_t e = run(ctx, LIONCUB_K_M1_PARTIAL, [&] { return launch_m1(q, 1, 0, ctx->stream); });
+  hipError_t e = run(ctx, LIONCUB_K_M1_PARTIAL, [&] { return launch_m1(q, 1, 0, 0, ctx->stream); });
   if (e == hipSuccess)
-    e = run(ctx, LIONCUB_K_M1_FINALIZE, [&] { return launch_m1_finalize(q, ctx->stream); });
+    e = run(ctx, LIONCUB_K_M1_FINALIZE, [&] { return launch_m1_finalize(q, 0, ctx->stream); });
   if (e == hipSuccess)
-    e = run(ctx, LIONCUB_K_QUANT, [&] { return launch_quant_codes(q, codes, ctx->stream); });
+    e = run(ctx, LIONCUB_K_QUANT, [&] { return launch_quant_codes(q, codes, 0, ctx->stream); });
+  return dev_status(e);
+}
+
+int lioncub_quant_linf(lioncub_ctx* ctx, const float* x, int64_t t, int8_t* codes,
+                       double* minf) {
+  if (!ctx || !x || !codes || t < 1) return LIONCUB_EINVAL;
+  if (ctx->cfg.qbits < 2 || ctx->cfg.qbits > 8) return LIONCUB_EINVAL;
+  if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(minf, 16)) return LIONCUB_EALIGN;
+  M1Params q;
+  fill_m1_params(ctx, &q);
+  q.x = x;
+  q.m1_out = minf;
+  q.t = t;
+  hipError_t e = run(ctx, LIONCUB_K_M1_PARTIAL, [&] { return launch_m1(q, 1, 0, 1, ctx->stream); });
+  if (e == hipSuccess)
+    e = run(ctx, LIONCUB_K_M1_FINALIZE, [&] { return launch_m1_finalize(q, 1, ctx->stream); });
+  if (e == hipSuccess)
+    e = run(ctx, LIONCUB_K_QUANT_LINF,
+            [&] { return launch_quant_codes(q, codes, 1, ctx->stream); });
   return dev_status(e);
 }
 

@@ -17,6 +17,9 @@
 // with parity zeros, Eq. (1), the quantised sum and global sign; selective
 // momentum synchronisation of the embedding and output layers), and the
 // D-Lion summary page ("Approach": per-worker momentum, majority vote).
+// The max-norm baseline (kAggLinf) is the L1 path with the codes rounded
+// stochastically against max |c|: the quantiser the Lion Cub page compares
+// Eq. (1) with (Figure 4).
 //
 // Workers are processed in batches of WB: all 2*WB loads of a batch are
 // issued before any use, which gives every wave 2*WB outstanding vector
@@ -114,6 +117,7 @@ __device__ __forceinline__ void step_block(const StepParams& p, const BlockEnt& 
   constexpr int Q = kRounds;
   const int W = WT > 0 ? WT : p.W;
   const int tid = threadIdx.x;
+  constexpr bool kQ = AGG == kAggL1 || AGG == kAggLinf;  // quantised paths
   const double* __restrict__ scl = p.scale + be.tensor;  // scl[i*nT]
   float* __restrict__ m = p.m;
 
@@ -124,6 +128,13 @@ __device__ __forceinline__ void step_block(const StepParams& p, const BlockEnt& 
     const int loc = kThreads * kQuad * q + kQuad * tid;
     j[q] = be.start + loc;
     nv[q] = FULL ? kQuad : max(0, min(kQuad, be.len - loc));
+  }
+  // max-norm draws: element j of worker i takes mix64(seed + ((t*W + i)*d +
+  // j + 1) * gamma) = mix64(zrow_i + j*gamma), wrapping mod 2^64
+  uint64_t jg[AGG == kAggLinf ? Q : 1];
+  if constexpr (AGG == kAggLinf) {
+#pragma unroll
+    for (int q = 0; q < Q; ++q) jg[q] = static_cast<uint64_t>(j[q]) * kGamma;
   }
 
   // theta does not change until the end: fetch it first
@@ -159,7 +170,7 @@ __device__ __forceinline__ void step_block(const StepParams& p, const BlockEnt& 
   // for all of them before its first product; an LDS read is counted apart
   // from the memory loads and arrives first.
   __shared__ double sh_sc[256];
-  if (AGG == kAggL1) {
+  if (kQ) {
     for (int i = tid; i < W; i += kThreads) sh_sc[i] = scl[static_cast<int64_t>(i) * p.nT];
     __syncthreads();
   }
@@ -168,7 +179,7 @@ __device__ __forceinline__ void step_block(const StepParams& p, const BlockEnt& 
 #pragma unroll 1
   for (int i0 = 0; i0 < W; i0 += WB) {
     double sc_b[WB];
-    if (AGG == kAggL1) {
+    if (kQ) {
 #pragma unroll
       for (int b = 0; b < WB; ++b) sc_b[b] = (kExact || i0 + b < W) ? sh_sc[i0 + b] : 0.0;
     }
@@ -191,7 +202,11 @@ __device__ __forceinline__ void step_block(const StepParams& p, const BlockEnt& 
     for (int b = 0; b < WB; ++b) {
       const int i = i0 + b;
       if (!kExact && i >= W) break;
-      const double s_i = AGG == kAggL1 ? sc_b[b] : 0.0;
+      const double s_i = kQ ? sc_b[b] : 0.0;
+      uint64_t zrow = 0;
+      if constexpr (AGG == kAggLinf)
+        zrow = p.seed + ((static_cast<uint64_t>(p.t) * static_cast<uint64_t>(W) +
+                          static_cast<uint64_t>(i)) * static_cast<uint64_t>(p.d) + 1u) * kGamma;
 #pragma unroll
       for (int q = 0; q < Q; ++q) {
         const int64_t idx = static_cast<int64_t>(i) * p.ld + j[q];
@@ -202,10 +217,16 @@ __device__ __forceinline__ void step_block(const StepParams& p, const BlockEnt& 
           const float c = (p.beta1 * mv[b][q].v[k]) + (p.omega1 * gv[b][q].v[k]);
           if (AGG == kAggVote || AGG == kAggAvg) {
             nib |= ((FULL || k < nv[q]) ? sign_bit(c, par) : 0u) << k;
-          } else if (AGG == kAggL1) {
-            double y = __builtin_rint(static_cast<double>(c) * s_i);
-            y = fmin(fmax(y, -static_cast<double>(p.qmax)), static_cast<double>(p.qmax));
-            const int qc = static_cast<int>(y);
+          } else if (kQ) {
+            int qc;
+            if constexpr (AGG == kAggLinf) {
+              qc = sr_code(c, s_i, static_cast<double>(p.qmax),
+                           mix64(zrow + jg[q] + static_cast<uint64_t>(k) * kGamma));
+            } else {
+              double y = __builtin_rint(static_cast<double>(c) * s_i);
+              y = fmin(fmax(y, -static_cast<double>(p.qmax)), static_cast<double>(p.qmax));
+              qc = static_cast<int>(y);
+            }
             sum[q][k] += qc;
             if (DBG) nib |= (static_cast<uint32_t>(qc) & 0xFFu) << (8 * k);
           }
@@ -226,7 +247,7 @@ __device__ __forceinline__ void step_block(const StepParams& p, const BlockEnt& 
             if ((tid & 15) == 0 && (FULL || nv[q] > 0))
               p.bits[static_cast<int64_t>(i) * (p.ld >> 6) + (j[q] >> 6)] = word;
           }
-        } else if (AGG == kAggL1 && DBG && p.codes && (FULL || nv[q] > 0)) {
+        } else if (kQ && DBG && p.codes && (FULL || nv[q] > 0)) {
           st_b4(p.codes + idx, nib, nv[q]);
         }
         if (FULL || nv[q] > 0) {
@@ -268,7 +289,7 @@ __device__ __forceinline__ void step_block(const StepParams& p, const BlockEnt& 
         sf[k] = static_cast<float>(net) / static_cast<float>(W);
       }
       if (DBG && p.counts) st_b4(p.counts + j[q], cnt[q], nv[q]);
-    } else if (AGG == kAggL1) {
+    } else if (kQ) {
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         s[k] = (sum[q][k] > 0) - (sum[q][k] < 0);
@@ -293,7 +314,9 @@ __device__ __forceinline__ void step_block(const StepParams& p, const BlockEnt& 
         for (int k = 0; k < 4; ++k) {
           if (!FULL && k >= nv[q]) break;
           const int ref = (csum[q][k] > 0.0f) - (csum[q][k] < 0.0f);
-          if (AGG != kAggL1 && 2 * static_cast<int>((cnt[q] >> (8 * k)) & 0xFFu) == W) st_tie++;
+          if ((AGG == kAggVote || AGG == kAggAvg) &&
+              2 * static_cast<int>((cnt[q] >> (8 * k)) & 0xFFu) == W)
+            st_tie++;
           if (s[k] != 0 && s[k] == ref) st_match++;
           if (s[k] != 0 && s[k] == -ref) st_flip++;
           if (s[k] == 0) st_zero++;
@@ -384,11 +407,13 @@ static hipError_t launch_t(const StepParams& p, int nblk, hipStream_t st) {
 hipError_t launch_step(const StepParams& p, int nblk, int theta_bf16, int grad_bf16, int agg,
                        hipStream_t st) {
   const bool dbg = p.bits || p.codes || p.counts || p.sums || p.sign || p.stats || p.mvar_max;
-  const int key = (theta_bf16 << 4) | (grad_bf16 << 3) | ((dbg ? 1 : 0) << 2) | agg;
+  if (agg < 0 || agg > kAggLinf) return hipErrorInvalidValue;
+  const int key = (theta_bf16 << 5) | (grad_bf16 << 4) | ((dbg ? 1 : 0) << 3) | agg;
   switch (key) {
 #define LC_CASE(TT, GT, D, A) \
-  case ((TT << 4) | (GT << 3) | (D << 2) | A): return launch_t<TT, GT, (D != 0), A>(p, nblk, st);
-#define LC_AGGS(TT, GT, D) LC_CASE(TT, GT, D, 0) LC_CASE(TT, GT, D, 1) LC_CASE(TT, GT, D, 2)
+  case ((TT << 5) | (GT << 4) | (D << 3) | A): return launch_t<TT, GT, (D != 0), A>(p, nblk, st);
+#define LC_AGGS(TT, GT, D) \
+  LC_CASE(TT, GT, D, 0) LC_CASE(TT, GT, D, 1) LC_CASE(TT, GT, D, 2) LC_CASE(TT, GT, D, 4)
     LC_AGGS(0, 0, 0) LC_AGGS(0, 0, 1) LC_AGGS(0, 1, 0) LC_AGGS(0, 1, 1)
     LC_AGGS(1, 0, 0) LC_AGGS(1, 0, 1) LC_AGGS(1, 1, 0) LC_AGGS(1, 1, 1)
     LC_CASE(0, 0, 0, 3) LC_CASE(0, 1, 0, 3) LC_CASE(1, 0, 0, 3) LC_CASE(1, 1, 0, 3)

@@ -66,7 +66,7 @@ enum {
 };
 
 enum { LIONCUB_F32 = 0, LIONCUB_BF16 = 1 };
-enum { LIONCUB_AGG_VOTE = 0, LIONCUB_AGG_L1SUM = 1, LIONCUB_AGG_AVG = 2 };
+enum { LIONCUB_AGG_VOTE = 0, LIONCUB_AGG_L1SUM = 1, LIONCUB_AGG_AVG = 2, LIONCUB_AGG_LINFSUM = 3 };
 enum { LIONCUB_TIE_PARITY = 0, LIONCUB_TIE_ZERO = 1 };
 
 typedef struct {
@@ -85,25 +85,33 @@ typedef struct {
   int32_t grad_dtype;            /* LIONCUB_F32 or LIONCUB_BF16; m is always fp32 */
   int32_t agg;                   /* LIONCUB_AGG_VOTE (majority vote of the sign
                                     bitmaps), LIONCUB_AGG_L1SUM (integer sum of
-                                    Eq. (1) codes) or LIONCUB_AGG_AVG (D-Lion
+                                    Eq. (1) codes), LIONCUB_AGG_AVG (D-Lion
                                     averaging: the applied update is the mean
-                                    of the W signs, (2*count - W) / W in fp32) */
-  int32_t qbits;                 /* n of Eq. (1), 2..8; required for L1SUM and for
-                                    lioncub_quant_l1, else ignored               */
+                                    of the W signs, (2*count - W) / W in fp32)
+                                    or LIONCUB_AGG_LINFSUM (integer sum of the
+                                    max-norm baseline's stochastic codes; see
+                                    lioncub_quant_linf)                         */
+  int32_t qbits;                 /* n of Eq. (1), 2..8; required for L1SUM,
+                                    LINFSUM, lioncub_quant_l1 and
+                                    lioncub_quant_linf, else ignored            */
   int32_t tie_mode;              /* vote ties (2*count == W): LIONCUB_TIE_PARITY
                                     (+1 odd t, -1 even t) or LIONCUB_TIE_ZERO (0) */
   float beta1, beta2, lr, wd;    /* finite                                       */
+  uint64_t sr_seed;              /* key of the stochastic rounding of the
+                                    max-norm codes (any value)                   */
 } lioncub_config;
 
 /* Optional per-element outputs of lioncub_step (each member may be NULL). */
 typedef struct {
   uint64_t *bits;  /* device [W][ld/64]: the workers' sign bitmaps (vote path)  */
-  int8_t *codes;   /* device [W][ld]: Eq. (1) codes (L1 path); j >= d untouched */
+  int8_t *codes;   /* device [W][ld]: Eq. (1) or max-norm codes (quantised
+                      paths); j >= d untouched                                 */
   uint8_t *counts; /* device [d]: number of +1 bits per element (vote path)     */
-  int32_t *sums;   /* device [d]: integer sum of the codes (L1 path)            */
+  int32_t *sums;   /* device [d]: integer sum of the codes (quantised paths)   */
   int8_t *sign;    /* device [d]: the global sign applied, in {-1, 0, +1}       */
-  double *m1;      /* device [W][n_tensors]: mean |c| per (worker, tensor)
-                      (L1 path); does not change which step kernel runs     */
+  double *m1;      /* device [W][n_tensors]: the norm the codes divide by per
+                      (worker, tensor): mean |c| (L1SUM) or max |c|
+                      (LINFSUM); does not change which step kernel runs     */
   /* Per-tensor diagnostics of this step (written, not accumulated).
    * Sources: the Lion Cub page's Figure 4 / Figure 11 (does the quantised
    * update's sign match or flip the unquantised one), its note on majority
@@ -137,11 +145,13 @@ int lioncub_set_stream(lioncub_ctx *ctx, void *hip_stream);
  *   m:     device [W][ld] fp32 (read, written; columns j >= d untouched)
  *   g:     device [W][ld], fp32 or bf16 per grad_dtype (read only)
  *   t:     1-based step index; decides zero and tie parity and averaging steps
- *   dbg:   NULL, or optional outputs (bits/counts on the vote path,
- *          codes/sums/m1 on the L1 path, sign on both); an output of the other
- *          path is an error (LIONCUB_EINVAL)
- * The vote path is one kernel; the L1 path is three (mean |c| block partials,
- * per-(worker, tensor) mean and scale, then the fused quantise-sum-apply). */
+ *   dbg:   NULL, or optional outputs (bits/counts on the vote and averaging
+ *          paths, codes/sums/m1 on the quantised paths, sign and the
+ *          diagnostics on all); an output of another path is an error
+ *          (LIONCUB_EINVAL)
+ * The vote path is one kernel; the quantised paths are three (norm block
+ * partials, per-(worker, tensor) norm and scale, then the fused
+ * quantise-sum-apply). */
 int lioncub_step(lioncub_ctx *ctx, void *theta, float *m, const void *g, int64_t t,
                  const lioncub_debug *dbg);
 
@@ -166,6 +176,24 @@ int lioncub_vote(lioncub_ctx *ctx, const uint64_t *bits, int64_t t, uint8_t *cou
  * ... then folds), then divided by the tensor's element count.  A tensor
  * with mean 0 gets all-zero codes.  Needs qbits in 2..8 in the config. */
 int lioncub_quant_l1(lioncub_ctx *ctx, const float *x, int8_t *codes, double *m1);
+
+/* The max-norm baseline Eq. (1) is measured against (Lion Cub page, pith.
+ * science review, Figure 4 caption and the referee report on Eq. (1): the
+ * standard max-normalised quantiser with stochastic rounding; its formula is
+ * not printed there, this is the reading taken):
+ *   q = clamp(floor(y) + [u < y - floor(y)], +-(2^(n-1)-1)),
+ *   y = (2^(n-1)-1) / max|x| * x in fp64 (scale 0 when max|x| == 0),
+ *   u = (r >> 11) * 2^-53, r = SplitMix64 output (t*W + i)*d + j of the
+ *   stream keyed by cfg.sr_seed, i.e. mix(sr_seed + (counter+1)*0x9E3779B97F4A7C15)
+ *   with Steele-Lea-Flood's mixer (shifts 30/27/31, multipliers
+ *   0xBF58476D1CE4E5B9 and 0x94D049BB133111EB), all mod 2^64.
+ * x[W][ld] (device fp32) -> codes[W][ld] (device int8, columns j >= d
+ * untouched) and, if minf != NULL, minf[W][n_tensors] (device fp64) = max |x|
+ * per (worker, tensor).  t >= 1 selects the draws (the fused step with
+ * LIONCUB_AGG_LINFSUM at step t draws the same ones for c).  Needs qbits in
+ * 2..8 in the config. */
+int lioncub_quant_linf(lioncub_ctx *ctx, const float *x, int64_t t, int8_t *codes,
+                       double *minf);
 
 /* ---- receive side and wire formats of the worker-sharded exchange -------
  * Sources: "Lion Cub: Minimizing Communication Overhead in Distributed Lion",
@@ -211,7 +239,8 @@ int lioncub_unpack_sum(lioncub_ctx *ctx, const uint32_t *wire, int32_t *sums, in
  * recorded).  lioncub_profile_end synchronises on the events, disables the
  * hook and writes, per kernel kind k (LIONCUB_K_*), the summed duration in
  * ms_total[k] and the launch count in launches[k] (arrays of
- * LIONCUB_K_COUNT entries, host memory). */
+ * LIONCUB_K_COUNT entries, host memory).  The norm pass of both quantised
+ * paths (mean |c| or max |c|) is counted as M1_PARTIAL and M1_FINALIZE. */
 enum {
   LIONCUB_K_VOTE_STEP = 0,
   LIONCUB_K_M1_PARTIAL = 1,
@@ -226,7 +255,9 @@ enum {
   LIONCUB_K_UNPACK_SUM = 10,
   LIONCUB_K_AVG_STEP = 11,
   LIONCUB_K_STATS = 12,
-  LIONCUB_K_COUNT = 13
+  LIONCUB_K_LINF_STEP = 13,
+  LIONCUB_K_QUANT_LINF = 14,
+  LIONCUB_K_COUNT = 15
 };
 int lioncub_profile_begin(lioncub_ctx *ctx, int32_t capacity);
 int lioncub_profile_end(lioncub_ctx *ctx, double *ms_total, int32_t *launches);

@@ -18,7 +18,8 @@ def lioncub_for(wl, **over):
     kw = dict(d=wl.d, W=wl.W, tensor_offsets=wl.offsets, ld=wl.ld,
               sync_m=wl.sync_flags if any(wl.sync_flags) else None, sync_every=wl.sync_every,
               theta_dtype=wl.theta_dtype, grad_dtype=wl.grad_dtype, agg=wl.agg,
-              qbits=wl.qbits, tie=wl.tie, beta1=wl.beta1, beta2=wl.beta2, lr=wl.lr, wd=wl.wd)
+              qbits=wl.qbits, tie=wl.tie, beta1=wl.beta1, beta2=wl.beta2, lr=wl.lr, wd=wl.wd,
+              sr_seed=wl.sr_seed)
     kw.update(over)
     return LionCub(**kw)
 
@@ -64,7 +65,7 @@ def check_float_state(name, got, want, bf16=False):
 def inject_zeros(wl, m, g, rs, frac=0.01):
     """Zero m and g at random (worker, element) spots so that c is exactly 0
     there (the parity rule), and all workers of some columns (ties at every
-    W), and one whole (worker, tensor) row on the L1 path (M1 = 0)."""
+    W), and one whole (worker, tensor) row on the quantised paths (norm 0)."""
     d = wl.d
     mask = rs.random((wl.W, d)) < frac
     m[:, :d][mask] = 0
@@ -72,7 +73,7 @@ def inject_zeros(wl, m, g, rs, frac=0.01):
     cols = rs.integers(0, d, max(1, d // 200))
     m[:, cols] = 0
     g[:, cols] = 0
-    if wl.agg == "l1" and wl.n_tensors > 1:
+    if wl.agg in ("l1", "linf") and wl.n_tensors > 1:
         a, b = wl.offsets[1], wl.offsets[2]
         m[wl.W - 1, a:b] = 0
         g[wl.W - 1, a:b] = 0

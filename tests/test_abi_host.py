@@ -69,7 +69,9 @@ def test_workspace_bytes_layout():
     dict(tensor_offsets=[64, 4096, 10000]),               # off[0] != 0
     dict(sync_every=0),
     dict(theta_dtype=2), dict(grad_dtype=-1),
-    dict(agg=3), dict(agg=_abi.AGG_L1SUM, qbits=1), dict(agg=_abi.AGG_L1SUM, qbits=9),
+    dict(agg=4), dict(agg=-1), dict(agg=_abi.AGG_L1SUM, qbits=1),
+    dict(agg=_abi.AGG_L1SUM, qbits=9), dict(agg=_abi.AGG_LINFSUM, qbits=0),
+    dict(agg=_abi.AGG_LINFSUM, qbits=9),
     dict(tie_mode=3),
     dict(lr=float("nan")), dict(beta1=float("inf")),
 ])

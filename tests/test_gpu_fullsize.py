@@ -4,7 +4,8 @@ column ranges (first, last -- the ragged end --, tensor boundaries and random
 interior ranges).  On the L1 workloads the oracle first recomputes M1 from
 the pre-step state, streamed from the device one worker row at a time, for
 every (worker, tensor) pair the samples touch (all of them for the flat 350M
-model), and M1 itself is compared bit for bit with the library's."""
+model), and M1 itself is compared bit for bit with the library's.  The
+max-norm baseline on the flat 350M shape does the same with max |c|."""
 import numpy as np
 import pytest
 
@@ -53,6 +54,20 @@ def oracle_m1(wl, m, g, pairs):
     return res
 
 
+def oracle_minf(wl, m, g, pairs):
+    """max |c|[i][T] for the requested pairs (a maximum: chunk order is free)."""
+    off = wl.offsets
+    res = {}
+    for (i, T) in pairs:
+        a, b = off[T], off[T + 1]
+        v = 0.0
+        for s in range(a, b, STREAM):
+            e = min(b, s + STREAM)
+            v = max(v, lco.minf(lco.c_row(wl, to_host(m[i, s:e]), to_host(g[i, s:e]))))
+        res[(i, T)] = v
+    return res
+
+
 def run_fullsize(wl, steps, tensors=None, n_random=6):
     import torch
     torch.cuda.set_device(0)
@@ -72,9 +87,9 @@ def run_fullsize(wl, steps, tensors=None, n_random=6):
                 to_host(g[:, j0:j1]).copy()) for j0, j1 in ranges]
         m1v = None
         dbg = None
-        if wl.agg == "l1":
+        if wl.agg in ("l1", "linf"):
             pairs = [(i, T) for i in range(wl.W) for T in tensors]
-            want_m1 = oracle_m1(wl, m, g, pairs)
+            want_m1 = (oracle_m1 if wl.agg == "l1" else oracle_minf)(wl, m, g, pairs)
             _say(wl.name, f"t={t} oracle M1 done for {len(pairs)} pairs")
             m1v = np.full((wl.W, wl.n_tensors), np.nan)
             for (i, T), v in want_m1.items():
@@ -109,6 +124,12 @@ def test_gpt2_124M_w8_vote_fullsize():
 
 def test_flat_350M_w16_l1q4_fullsize():
     run_fullsize(wls.FLAT_350M_W16_L1Q4, steps=[1, 2])
+
+
+def test_flat_350M_w16_linfq4_fullsize():
+    """The max-norm baseline at the flat 350M, W=16, n=4 shape."""
+    wl = wls.FLAT_350M_W16_L1Q4.with_(name="flat-350M-w16-linfq4", agg="linf")
+    run_fullsize(wl, steps=[3])
 
 
 def test_gpt_760M_w8_vote_bf16_sync_fullsize():

@@ -420,3 +420,113 @@ def test_p_bit_path_composes_into_the_step():
     torch.cuda.synchronize()
     assert torch.equal(sums, dbg["sums"]) and torch.equal(sign, dbg["sign"])
     lc.close()
+
+
+# ------------------------------- max-norm stochastic baseline (Q-inf) -----
+# Parity here is bit-exact against the oracle's reading of the quantiser
+# (the pages name it but do not print its formula).
+
+LINF = {
+    "linf-flat-W16-q4": wls.FLAT_350M_W16_L1Q4.with_(tensors=[("flat", 70 * 4096 + 896)],
+                                                     agg="linf"),
+    "linf-gpt-W8-q8-bf16g(small)": small(wls.GPT_1B3_W8_L1Q8, 2 * 4096 + 320, 30).with_(
+        agg="linf"),
+    "linf-ragged-W5-q3": wls.flat("i1", 2 * 4096 + 4099, W=5, agg="linf", qbits=3),
+    "linf-W1-q2": wls.flat("i2", 5000, W=1, agg="linf", qbits=2),
+    "linf-W255-q8": wls.flat("i3", 1000, W=255, agg="linf", qbits=8),
+    "linf-sync-every-2-bf16": wls.Workload(name="i4", tensors=[("wte", 4096 + 64), ("h", 128),
+                                                               ("wpe", 64)], W=3, agg="linf",
+                                           qbits=4, sync_names=("wte", "wpe"), sync_every=2,
+                                           theta_dtype="bf16", grad_dtype="bf16"),
+    "linf-tiny-tensors-W8": wls.Workload(name="i5", tensors=[("a", 64), ("b", 4096),
+                                                             ("c", 4160), ("d", 64)], W=8,
+                                         agg="linf", qbits=4, sr_seed=2**64 - 1),
+    "linf-row-padding-W16": wls.flat("i6", 5000, W=16, agg="linf", qbits=4, ld_pad=192),
+    "linf-W4-generic-bf16g": wls.flat("i7", 3 * 4096 + 4, W=4, agg="linf", qbits=5,
+                                      grad_dtype="bf16"),
+}
+
+
+@pytest.mark.parametrize("debug", [True, False], ids=["debug", "production"])
+@pytest.mark.parametrize("name", list(LINF))
+def test_linf_parity(name, debug):
+    wl = LINF[name]
+    res = gpu_step_vs_oracle(wl, steps=3, debug=debug)
+    print(name, res, flush=True)
+
+
+def test_linf_counter_wraps_like_the_oracle():
+    """Step indices near 2^62: (t*W + i)*d wraps mod 2^64 on both sides."""
+    wl = wls.flat("iw", 2 * 4096 + 64, W=3, agg="linf", qbits=4)
+    res = gpu_step_vs_oracle(wl, steps=2, t0=2**62 + 5, debug=True)
+    print(res, flush=True)
+
+
+def _quant_linf_case(x, tensors, qbits, t, seed=0x5EED):
+    import torch
+    W, ld = x.shape
+    wl = wls.Workload(name="qi", tensors=tensors, W=W, agg="linf", qbits=qbits, sr_seed=seed)
+    wl = wl.with_(ld_pad=ld - wl.ld)
+    lc = lioncub_for(wl)
+    codes = torch.full((W, ld), 99, dtype=torch.int8, device="cuda")
+    mv = torch.zeros((W, wl.n_tensors), dtype=torch.float64, device="cuda")
+    lc.quant_linf(to_dev(x), t, codes, mv)
+    torch.cuda.synchronize()
+    wc, wm = lco.quant_linf(wl, x, t)
+    gm = to_host(mv)
+    assert np.array_equal(gm.view(np.uint64), wm.view(np.uint64)), (gm, wm)
+    gc = to_host(codes)
+    assert np.array_equal(gc[:, : wl.d], wc[:, : wl.d])
+    assert np.all(gc[:, wl.d:] == 99)           # columns past d untouched
+    lc.close()
+    return gc[:, : wl.d]
+
+
+@pytest.mark.parametrize("qbits", [2, 4, 8])
+@pytest.mark.parametrize("t", [1, 2, 2**62 + 1])
+def test_quant_linf_student_t(qbits, t):
+    rs = np.random.default_rng(qbits)
+    tensors = [("a", 9 * 4096 + 320), ("z", 128), ("b", 64)]
+    d = sum(n for _, n in tensors)
+    x = (rs.standard_t(2.5, (16, d)) * 1e-3).astype(np.float32)
+    x[:, 9 * 4096 + 320: 9 * 4096 + 448] = 0.0               # a tensor of zeros
+    codes = _quant_linf_case(x, tensors, qbits, t)
+    if qbits <= 4:                                            # most codes 0 on heavy tails
+        assert np.mean(codes[:, : 9 * 4096 + 320] == 0) > 0.5
+
+
+def test_quant_linf_adversarial_magnitudes():
+    """Magnitudes over 1e-30..1e30, subnormals, more than 64 blocks."""
+    rs = np.random.default_rng(17)
+    tensors = [("a", 70 * 4096 + 832), ("s", 4096 + 64)]
+    d = sum(n for _, n in tensors)
+    W, ld = 3, (d + 63) // 64 * 64
+    x = (10.0 ** rs.uniform(-30, 30, (W, ld)) * np.where(rs.random((W, ld)) < 0.5, -1, 1))
+    x = x.astype(np.float32)
+    a = tensors[0][1]
+    x[1, a:d] = (rs.integers(1, 100, d - a) * 1e-45).astype(np.float32)
+    _quant_linf_case(x, tensors, 4, 3, seed=12345)
+
+
+def test_linf_step_codes_are_quant_linf_of_c():
+    """The fused step's codes at step t are quant_linf(c, t) on the device."""
+    import torch
+    from synth import gen
+    wl = wls.Workload(name="ic", tensors=[("a", 2 * 4096 + 192), ("b", 4096)], W=8,
+                      agg="linf", qbits=4, grad_dtype="bf16")
+    theta, m = gen.host_theta(wl), gen.host_m(wl)
+    g = gen.host_g(wl, 7)
+    c = np.zeros((wl.W, wl.ld), np.float32)
+    for i in range(wl.W):
+        c[i, : wl.d] = lco.c_row(wl, m[i, : wl.d], g[i, : wl.d])
+    lc = lioncub_for(wl)
+    dbg = {"codes": torch.zeros((wl.W, wl.ld), dtype=torch.int8, device="cuda"),
+           "m1": torch.zeros((wl.W, wl.n_tensors), dtype=torch.float64, device="cuda")}
+    lc.step(to_dev(theta), to_dev(m), to_dev(g, True), 7, dbg)
+    codes = torch.zeros((wl.W, wl.ld), dtype=torch.int8, device="cuda")
+    mv = torch.zeros((wl.W, wl.n_tensors), dtype=torch.float64, device="cuda")
+    lc.quant_linf(to_dev(c), 7, codes, mv)
+    torch.cuda.synchronize()
+    assert torch.equal(codes[:, : wl.d], dbg["codes"][:, : wl.d])
+    assert torch.equal(mv, dbg["m1"])
+    lc.close()
