@@ -53,6 +53,12 @@ class LionCub:
         self.stream = stream if stream is not None else torch.cuda.current_stream(device)
         self.ctx = lioncub_init(self.cfg, _abi._stream_handle(self.stream), self.workspace)
 
+    def set_stream(self, stream):
+        """Enqueue later calls on `stream` (a torch.cuda.Stream), e.g. the
+        capturing stream of a torch.cuda.graph."""
+        lioncub_set_stream(self.ctx, _abi._stream_handle(stream))
+        self.stream = stream
+
     def step(self, theta, m, g, t, debug=None):
         lioncub_step(self.ctx, theta, m, g, t, debug)
 

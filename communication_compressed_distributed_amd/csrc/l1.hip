@@ -193,22 +193,35 @@ __global__ __launch_bounds__(kThreads) void k_m1_partial(M1Params p) {
   }
 }
 
-// Group values: one workgroup per (worker, group of 256 consecutive block
-// partials of one tensor); lane l takes partial l (0.0 past the tensor's last
-// block), each wave folds, then (w0+w1)+(w2+w3).
+// Group values: one workgroup per group of 256 consecutive block partials
+// of one tensor, for all W workers; for worker i, lane l takes partial l of
+// the group (0.0 past the tensor's last block), each wave folds, then
+// (w0+w1)+(w2+w3).  Thread l reads block l's W partials, one contiguous run
+// of the block-major array, so each partial is fetched from HBM once.
 template <bool MX>
 __global__ __launch_bounds__(kThreads) void k_m1_group(M1Params p) {
-  __shared__ double sh[4];
+  __shared__ double sh[4][256];  // [wave][worker]
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int64_t gid = blockIdx.x;
-  const int i = static_cast<int>(gid / p.ngrp), gg = static_cast<int>(gid % p.ngrp);
+  const int gg = blockIdx.x;
   const GroupEnt ge = p.grp[gg];
-  double v = tid < ge.cnt ? p.partial[static_cast<int64_t>(ge.blk + tid) * p.W + i] : 0.0;
-  v = wave_fold<MX>(v);
-  if (lane == 0) sh[wave] = v;
+  const double* __restrict__ row = p.partial + static_cast<int64_t>(ge.blk + tid) * p.W;
+  const bool have = tid < ge.cnt;
+#pragma unroll 1
+  for (int i0 = 0; i0 < p.W; i0 += 4) {
+    double v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = (have && i0 + u < p.W) ? row[i0 + u] : 0.0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (i0 + u >= p.W) break;  // uniform
+      const double f = wave_fold<MX>(v[u]);
+      if (lane == 0) sh[wave][i0 + u] = f;
+    }
+  }
   __syncthreads();
-  if (tid == 0)
-    p.gval[static_cast<int64_t>(i) * p.ngrp + gg] = red<MX>(red<MX>(sh[0], sh[1]), red<MX>(sh[2], sh[3]));
+  for (int i = tid; i < p.W; i += kThreads)
+    p.gval[static_cast<int64_t>(i) * p.ngrp + gg] =
+        red<MX>(red<MX>(sh[0][i], sh[1][i]), red<MX>(sh[2][i], sh[3][i]));
 }
 
 // One wave per (worker, tensor): lane l sums group values l, l+64, ... in
@@ -297,8 +310,7 @@ hipError_t launch_m1(const M1Params& p, int src_x, int grad_bf16, int maxnorm, h
 }
 
 hipError_t launch_m1_finalize(const M1Params& p, int maxnorm, hipStream_t st) {
-  const int64_t groups = static_cast<int64_t>(p.W) * p.ngrp;
-  const dim3 gg(static_cast<unsigned>(groups)), b(kThreads);
+  const dim3 gg(static_cast<unsigned>(p.ngrp)), b(kThreads);
   if (maxnorm) hipLaunchKernelGGL(k_m1_group<true>, gg, b, 0, st, p);
   else hipLaunchKernelGGL(k_m1_group<false>, gg, b, 0, st, p);
   const hipError_t e = hipGetLastError();

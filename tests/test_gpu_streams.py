@@ -1,0 +1,110 @@
+"""Streams and graphs.  The library enqueues only on its context's stream
+and allocates nothing per call, so a context can run on a side stream, two
+contexts can run on two streams at once, and a whole step (the L1 path's
+three kernels, or the vote kernel) can be captured into a HIP graph and
+replayed.  Every result is compared with the CPU oracle bit for bit."""
+import numpy as np
+import pytest
+
+from oracle import lco
+from synth import gen
+from synth import workloads as wls
+from tests.harness import check_float_state, lioncub_for, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+def _host_state(wl):
+    return gen.host_theta(wl), gen.host_m(wl)
+
+
+def _check(wl, d_theta, d_m, theta, m, what):
+    check_float_state(f"theta {what}", to_host(d_theta), theta, bf16=wl.theta_dtype == "bf16")
+    check_float_state(f"m {what}", to_host(d_m)[:, : wl.d], m[:, : wl.d])
+
+
+def test_context_on_a_side_stream():
+    import torch
+    wl = wls.flat("ss", 3 * 4096 + 100, W=8, agg="l1", qbits=4)
+    theta, m = _host_state(wl)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        lc = lioncub_for(wl, stream=s)
+        d_theta, d_m = to_dev(theta), to_dev(m)
+        for t in (1, 2):
+            g = gen.host_g(wl, t)
+            lc.step(d_theta, d_m, to_dev(g), t)
+            lco.step(wl, theta, m, g, t)
+    s.synchronize()
+    _check(wl, d_theta, d_m, theta, m, "side stream")
+    lc.close()
+
+
+def test_two_contexts_on_two_streams_at_once():
+    import torch
+    wa = wls.flat("sa", 4 * 4096 + 64, W=4, theta_dtype="bf16", grad_dtype="bf16")
+    wb = wls.Workload(name="sb", tensors=[("x", 2 * 4096 + 320), ("y", 4096)], W=16, agg="l1",
+                      qbits=4)
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    ha, hb = _host_state(wa), _host_state(wb)
+    ga = [gen.host_g(wa, t) for t in (1, 2, 3)]
+    gb = [gen.host_g(wb, t) for t in (1, 2, 3)]
+    da = (to_dev(ha[0], True), to_dev(ha[1]), [to_dev(x, True) for x in ga])
+    db = (to_dev(hb[0]), to_dev(hb[1]), [to_dev(x) for x in gb])
+    torch.cuda.synchronize()
+    la, lb = lioncub_for(wa, stream=sa), lioncub_for(wb, stream=sb)
+    for k, t in enumerate((1, 2, 3)):          # interleaved launches on two streams
+        with torch.cuda.stream(sa):
+            la.step(da[0], da[1], da[2][k], t)
+        with torch.cuda.stream(sb):
+            lb.step(db[0], db[1], db[2][k], t)
+    torch.cuda.synchronize()
+    for k, t in enumerate((1, 2, 3)):
+        lco.step(wa, ha[0], ha[1], ga[k], t)
+        lco.step(wb, hb[0], hb[1], gb[k], t)
+    _check(wa, da[0], da[1], ha[0], ha[1], "stream a")
+    _check(wb, db[0], db[1], hb[0], hb[1], "stream b")
+    la.close()
+    lb.close()
+
+
+@pytest.mark.parametrize("agg", ["vote", "l1", "linf"])
+def test_step_captured_in_a_graph_and_replayed(agg):
+    """Capture one step at a fixed t, replay it three times with eager steps
+    of another context and host synchronisations in between; every replay
+    must equal the oracle's step from the previous state."""
+    import torch
+    wl = wls.Workload(name="gr", tensors=[("a", 5 * 4096 + 192), ("b", 4096 + 64)], W=8,
+                      agg=agg, qbits=0 if agg == "vote" else 4, sync_names=("b",),
+                      sync_every=3)
+    theta, m = _host_state(wl)
+    g = gen.host_g(wl, 3)
+    t = 3                                      # an averaging step for tensor b
+    d_theta, d_m, d_g = to_dev(theta), to_dev(m), to_dev(g)
+    lc = lioncub_for(wl)
+    # eager side work: a second context stepping its own copy of the state
+    e_theta, e_m = to_dev(theta), to_dev(m)
+    le = lioncub_for(wl)
+    h_theta, h_m = theta.copy(), m.copy()
+    torch.cuda.synchronize()
+
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        lc.set_stream(torch.cuda.current_stream())
+        lc.step(d_theta, d_m, d_g, t)
+    lc.set_stream(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    _check(wl, d_theta, d_m, theta, m, "after capture (nothing ran)")
+
+    for rep in range(3):
+        graph.replay()
+        torch.cuda.synchronize()
+        lco.step(wl, theta, m, g, t)
+        _check(wl, d_theta, d_m, theta, m, f"replay {rep}")
+        le.step(e_theta, e_m, d_g, t)          # eager work between replays
+        torch.cuda.synchronize()
+        lco.step(wl, h_theta, h_m, g, t)
+        _check(wl, e_theta, e_m, h_theta, h_m, f"eager {rep}")
+    del graph
+    lc.close()
+    le.close()
