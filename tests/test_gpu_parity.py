@@ -530,3 +530,20 @@ def test_linf_step_codes_are_quant_linf_of_c():
     assert torch.equal(codes[:, : wl.d], dbg["codes"][:, : wl.d])
     assert torch.equal(mv, dbg["m1"])
     lc.close()
+
+
+# ------------------------------------------------- more edges, all paths --
+
+@pytest.mark.parametrize("agg", ["l1", "linf"])
+@pytest.mark.parametrize("n", [2, 3, 4, 5, 6, 7, 8])
+def test_every_code_width_on_the_step(agg, n):
+    wl = wls.flat(f"n{n}", 2 * 4096 + 33, W=5, agg=agg, qbits=n, grad_dtype="bf16")
+    gpu_step_vs_oracle(wl, steps=2, debug=True)
+
+
+@pytest.mark.parametrize("agg", ["vote", "avg", "l1", "linf"])
+@pytest.mark.parametrize("d,W", [(1, 3), (1, 2), (63, 7), (64, 1), (65, 16)])
+def test_tiny_vectors(agg, d, W):
+    wl = wls.flat("tiny", d, W=W, agg=agg, qbits=0 if agg in ("vote", "avg") else 4)
+    gpu_step_vs_oracle(wl, steps=3, debug=True)
+    gpu_step_vs_oracle(wl, steps=1, debug=False, seed_shift=1)
