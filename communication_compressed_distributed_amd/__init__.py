@@ -7,7 +7,7 @@ the workers are aggregated by majority vote or integer sum, and the global
 sign updates the parameters and each worker's momentum.  `_abi` mirrors the C
 entry points; `LionCub` keeps a context and its workspace together.
 """
-from . import _abi
+from . import _abi, _checks
 from ._abi import (AGG_AVG, AGG_L1SUM, AGG_LINFSUM, AGG_VOTE, BF16, F32, TIE_PARITY, TIE_ZERO,
                    LionCubError, lioncub_apply, lioncub_destroy, lioncub_init, lioncub_pack,
                    lioncub_pack_codes, lioncub_profile_begin, lioncub_profile_end,
@@ -46,10 +46,13 @@ class LionCub:
             tie_mode=TIE_ZERO if tie == "zero" else TIE_PARITY,
             beta1=beta1, beta2=beta2, lr=lr, wd=wd, sr_seed=sr_seed)
         self.d, self.ld, self.W, self.n_tensors = d, ld, W, len(offs) - 1
+        self.spec = _checks.Spec(d=d, ld=ld, W=W, n_tensors=len(offs) - 1,
+                                 theta_dtype=theta_dtype, grad_dtype=grad_dtype, qbits=qbits)
         nbytes = lioncub_workspace_bytes(self.cfg)
         if nbytes == 0:
             raise LionCubError("lioncub_workspace_bytes", _abi.EINVAL)
         self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        self.device = self.workspace.device
         self.stream = stream if stream is not None else torch.cuda.current_stream(device)
         self.ctx = lioncub_init(self.cfg, _abi._stream_handle(self.stream), self.workspace)
 
@@ -59,31 +62,43 @@ class LionCub:
         lioncub_set_stream(self.ctx, _abi._stream_handle(stream))
         self.stream = stream
 
+    # Every method checks its tensors on the host (_checks) before passing
+    # their pointers: the C ABI cannot see a buffer's extent.
+
     def step(self, theta, m, g, t, debug=None):
+        _checks.step(self.spec, self.device, theta, m, g, debug)
         lioncub_step(self.ctx, theta, m, g, t, debug)
 
     def pack(self, x, t, bits):
+        _checks.pack(self.spec, self.device, x, bits)
         lioncub_pack(self.ctx, x, t, bits)
 
     def vote(self, bits, t, counts=None, sign=None):
+        _checks.vote(self.spec, self.device, bits, counts, sign)
         lioncub_vote(self.ctx, bits, t, counts, sign)
 
     def quant_l1(self, x, codes, m1=None):
+        _checks.quant(self.spec, self.device, x, codes, m1)
         lioncub_quant_l1(self.ctx, x, codes, m1)
 
     def quant_linf(self, x, t, codes, minf=None):
+        _checks.quant(self.spec, self.device, x, codes, minf)
         lioncub_quant_linf(self.ctx, x, t, codes, minf)
 
     def vote_bits(self, bits, t, sign_bits, zero_bits=None):
+        _checks.vote_bits(self.spec, self.device, bits, sign_bits, zero_bits)
         lioncub_vote_bits(self.ctx, bits, t, sign_bits, zero_bits)
 
     def apply(self, theta, m, g, t, sign_bits, zero_bits=None):
+        _checks.apply(self.spec, self.device, theta, m, g, sign_bits, zero_bits)
         lioncub_apply(self.ctx, theta, m, g, t, sign_bits, zero_bits)
 
     def pack_codes(self, codes, wire):
+        _checks.pack_codes(self.spec, self.device, codes, wire)
         lioncub_pack_codes(self.ctx, codes, wire)
 
     def unpack_sum(self, wire, sums=None, sign=None):
+        _checks.unpack_sum(self.spec, self.device, wire, sums, sign)
         lioncub_unpack_sum(self.ctx, wire, sums, sign)
 
     def profile_begin(self, capacity):

@@ -239,14 +239,22 @@ def test_deterministic_and_checkpoint_resume():
 
 def test_bad_arguments_on_device():
     import torch
-    from communication_compressed_distributed_amd import LionCubError
+    from communication_compressed_distributed_amd import LionCubError, _abi
     wl, lc = _ctx(4, 4096)
     th = torch.zeros(4096, device="cuda")
     m = torch.zeros((4, 4096), device="cuda")
     with pytest.raises(LionCubError):
         lc.step(th, m, m, 0)                              # t must be >= 1
-    with pytest.raises(LionCubError):
-        lc.step(th[1:], m, m, 1)                          # misaligned theta
+    with pytest.raises(LionCubError):                      # misaligned theta, raw ABI
+        _abi.lioncub_step(lc.ctx, th[1:], m, m, 1)
+    with pytest.raises(ValueError):                       # too short: caught on the host
+        lc.step(th[1:], m, m, 1)
+    with pytest.raises(ValueError):
+        lc.step(th, m[:, :2048], m, 1)                    # strided view of m
+    with pytest.raises(ValueError):
+        lc.step(th, m, m.to(torch.bfloat16), 1)           # g dtype differs from the config
+    with pytest.raises(ValueError):
+        lc.step(th.cpu(), m, m, 1)                        # host tensor
     with pytest.raises(LionCubError):
         lc.step(th, m, m, 1, {"codes": torch.zeros((4, 4096), dtype=torch.int8,
                                                    device="cuda")})  # L1 output on vote path
