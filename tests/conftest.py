@@ -1,3 +1,4 @@
+import json
 import os
 import sys
 
@@ -20,3 +21,14 @@ def oracle():
         build.build()
     lco.lib()
     return lco
+
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def golden(name):
+    """A cited fixture from tests/golden/ (values worked by hand from the
+    pages' definitions, stated on the pages, or published with a method the
+    code uses; never produced by the library)."""
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)

@@ -8,6 +8,7 @@ import pytest
 
 from oracle import lco
 from synth import workloads as wls
+from tests.conftest import golden
 from tests.harness import gpu_step_vs_oracle, lioncub_for, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
@@ -76,9 +77,10 @@ def test_edge_parity(name, debug):
 def test_vote_tie_rate_on_gpu():
     """Majority ties at W=4 occur for over 30% of parameters (the pages'
     observation; C(4,2)/16 = 0.375 for symmetric iid c)."""
+    gd = golden("tie_rate.json")
     res = gpu_step_vs_oracle(wls.FLAT_1M_W4_VOTE, steps=1, zeros=False)
     rate = res["ties"] / wls.FLAT_1M_W4_VOTE.d
-    assert abs(rate - 0.375) < 0.005
+    assert abs(rate - gd["closed_form"]["4"]) < 0.005 and rate > gd["W4_min_rate"]
 
 
 # ------------------------------------------------ standalone entry points --
@@ -90,20 +92,15 @@ def _ctx(W, d, ld=None, **kw):
     return wl, lioncub_for(wl)
 
 
-B1_X = np.array([
-    [0.5, -0.1, 0.0, 2.0, -3.0, 0.0, 1e-9, -1e-9],
-    [0.2, 0.3, -0.4, -2.0, -1.0, 0.0, 0.0, 0.7],
-    [-0.1, 0.2, 0.0, 1.0, 0.5, 0.0, -2.0, 0.1],
-    [-0.3, -0.5, 0.1, -1.0, -0.2, 0.0, 0.3, 0.0],
-], dtype=np.float32)
-
-
 @pytest.mark.parametrize("t,tie", [(1, "parity"), (2, "parity"), (1, "zero"), (2, "zero")])
 def test_pack_vote_handworked(t, tie):
+    """tests/golden/pack_vote_w4_d8.json through the library: bytes, counts
+    and signs equal both the hand-worked values and the oracle."""
     import torch
+    gd = golden("pack_vote_w4_d8.json")
     wl, lc = _ctx(4, 8, tie=tie)
     x = np.zeros((4, 64), np.float32)
-    x[:, :8] = B1_X
+    x[:, :8] = np.array(gd["x"], np.float32)
     bits = torch.full((4, 1), -1, dtype=torch.int64, device="cuda")
     lc.pack(to_dev(x), t, bits)
     counts = torch.zeros(8, dtype=torch.uint8, device="cuda")
@@ -115,6 +112,10 @@ def test_pack_vote_handworked(t, tie):
     wc, ws = lco.vote(want_bits, 4, 8, t, lco.TIE_ZERO if tie == "zero" else lco.TIE_PARITY)
     assert np.array_equal(to_host(counts), wc)
     assert np.array_equal(to_host(sign), ws)
+    want = gd["steps"][str(t)]
+    assert [int(w) for w in to_host(bits)[:, 0]] == want["bytes"]
+    assert to_host(counts).tolist() == want["counts"]
+    assert to_host(sign).tolist() == want["sign_zero" if tie == "zero" else "sign_parity"]
     lc.close()
 
 

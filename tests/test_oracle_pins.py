@@ -17,6 +17,7 @@ import pytest
 
 from synth import workloads as wls
 from synth.gen import bf16_bits_to_f32
+from tests.conftest import golden
 
 
 def one_tensor(d, W, **kw):
@@ -63,33 +64,22 @@ def test_bit_rule_zero_parity(oracle):
         assert oracle.bit(-0.0, t) == z
 
 
-# Hand-worked from the definitions (W=4, d=8).  t=1: zeros -> 1; t=2: zeros -> 0.
-B1_X = np.array([
-    [0.5, -0.1, 0.0, 2.0, -3.0, 0.0, 1e-9, -1e-9],
-    [0.2, 0.3, -0.4, -2.0, -1.0, 0.0, 0.0, 0.7],
-    [-0.1, 0.2, 0.0, 1.0, 0.5, 0.0, -2.0, 0.1],
-    [-0.3, -0.5, 0.1, -1.0, -0.2, 0.0, 0.3, 0.0],
-], dtype=np.float32)
-B1 = {
-    1: dict(bytes=[0x6D, 0xE3, 0xBE, 0xE4], counts=[2, 2, 3, 2, 1, 4, 3, 3],
-            parity=[1, 1, 1, 1, -1, 1, 1, 1], zero=[0, 0, 1, 0, -1, 1, 1, 1]),
-    2: dict(bytes=[0x49, 0x83, 0x9A, 0x44], counts=[2, 2, 1, 2, 1, 0, 2, 2],
-            parity=[-1] * 8, zero=[0, 0, -1, 0, -1, -1, 0, 0]),
-}
-
-
 @pytest.mark.parametrize("t", [1, 2])
 def test_pack_vote_handworked(oracle, t):
+    """tests/golden/pack_vote_w4_d8.json: bytes, counts and signs worked by
+    hand (W=4, d=8; t=1: zeros -> 1, t=2: zeros -> 0)."""
+    gd = golden("pack_vote_w4_d8.json")
+    want = gd["steps"][str(t)]
     x = np.zeros((4, 64), dtype=np.float32)
-    x[:, :8] = B1_X
+    x[:, :8] = np.array(gd["x"], dtype=np.float32)
     bits = oracle.pack(x, 8, t)
     assert bits.shape == (4, 1)
-    assert [int(w) for w in bits[:, 0]] == B1[t]["bytes"]
+    assert [int(w) for w in bits[:, 0]] == want["bytes"]
     counts, sign = oracle.vote(bits, 4, 8, t, oracle.TIE_PARITY)
-    assert counts.tolist() == B1[t]["counts"]
-    assert sign.tolist() == B1[t]["parity"]
+    assert counts.tolist() == want["counts"]
+    assert sign.tolist() == want["sign_parity"]
     counts, sign = oracle.vote(bits, 4, 8, t, oracle.TIE_ZERO)
-    assert sign.tolist() == B1[t]["zero"]
+    assert sign.tolist() == want["sign_zero"]
 
 
 @pytest.mark.parametrize("t", [1, 2])
@@ -178,7 +168,8 @@ def test_lion_closed_form_identical_workers(oracle, agg):
         np.testing.assert_allclose(m[i, :d], m_cf, rtol=2e-6)
     # the worked value theta_0 = 0.02, g > 0 after 10 steps of these hyperparameters
     if gv[0] > 0:
-        assert abs(theta[0] - 0.0189980450888024) < 1e-8
+        gd = golden("lion_closed_form.json")
+        assert abs(theta[0] - gd["theta_10"]) < gd["theta_10_tol"]
 
 
 def test_vote_single_worker_is_lion(oracle):
@@ -213,7 +204,7 @@ def test_sign_flip_step_closed_form(oracle):
     t_flip = 1 + math.floor(math.log(ratio) / math.log(b2)) + 1
     assert signs[: t_flip - 1] == [1] * (t_flip - 1)
     assert signs[t_flip - 1:] == [-1] * (steps - t_flip + 1)
-    assert t_flip == 294
+    assert t_flip == golden("lion_closed_form.json")["sign_flip_step"]
     # theta closed form: theta_T = a^T theta_0 - lr * sum_t a^(T-t) s_t
     lr, wd = float(np.float32(1e-4)), float(np.float32(0.1))
     a = 1 - lr * wd
@@ -264,17 +255,15 @@ def _quant_one(oracle, x, n):
 
 
 def test_quant_l1_handworked(oracle):
-    """Eq. (1) worked by hand, including products that land exactly on .5,
-    which pin round-half-to-even against round-half-away."""
-    codes, M = _quant_one(oracle, [0.5, -0.1, 0, 2, -3, 0.25, 0.05, -0.05], 4)
-    assert codes == [5, -1, 0, 7, -7, 2, 0, 0]
-    assert abs(M - 0.743750000372529) < 1e-15
-    codes, M = _quant_one(oracle, [0.5, -0.5, 1.5, -1.5], 2)
-    assert (codes, M) == ([0, 0, 1, -1], 1.0)              # half-away: [1,-1,1,-1]
-    codes, M = _quant_one(oracle, [0.5, 1.5, 2.5, -2.5, 8.0], 3)
-    assert (codes, M) == ([0, 2, 2, -2, 3], 3.0)           # half-away: [1,2,3,-3,3]
-    codes, M = _quant_one(oracle, [0.0, -0.0, 0.0, 0.0], 4)
-    assert (codes, M) == ([0, 0, 0, 0], 0.0)
+    """tests/golden/eq1_codes.json: Eq. (1) worked by hand, including products
+    that land exactly on .5, which pin round-half-to-even against
+    round-half-away."""
+    for case in golden("eq1_codes.json")["cases"]:
+        codes, M = _quant_one(oracle, case["x"], case["n"])
+        assert codes == case["codes"], case
+        assert abs(M - case["m1"]) <= case["m1_tol"], case
+        if "half_away" in case:
+            assert codes != case["half_away"]
 
 
 def _nearest_even(y: Fraction) -> int:
@@ -381,23 +370,23 @@ def test_m1_block_reads_past_n_as_zero(oracle):
 # ------------------------------------------------ integer sum and sign ----
 
 def test_l1_sum_handworked(oracle):
-    """W=2, n=2, one 4-element tensor.  With b1 = 0.5 and m = 0, c = g/2
-    exactly and Q1 is scale-free, so the codes are those of g:
+    """tests/golden/l1_sum_w2_n2.json: W=2, n=2, one 4-element tensor.  With
+    b1 = 0.5 and m = 0, c = g/2 exactly and Q1 is scale-free, so the codes
+    are those of g:
       w0 = [0.5, -0.5, 1.5, -1.5]: M1 = 1, codes [0, 0, 1, -1]
       w1 = [1, -3, -1, 1]:        M1 = 1.5, codes [1, -1, -1, 1]
     S = [1, -1, 0, 0] -> sign [+1, -1, 0, 0]; a zero sign only decays theta."""
-    wl = one_tensor(4, 2, agg="l1", qbits=2, beta1=0.5)
-    theta = np.array([0.02, 0.02, 0.02, -0.3], np.float32)
+    gd = golden("l1_sum_w2_n2.json")
+    wl = one_tensor(4, gd["W"], agg="l1", qbits=gd["n"], beta1=gd["beta1"])
+    theta = np.array(gd["theta"], np.float32)
     th0 = theta.copy()
     m = np.zeros((2, 64), np.float32)
     g = np.zeros((2, 64), np.float32)
-    g[0, :4] = [0.5, -0.5, 1.5, -1.5]
-    g[1, :4] = [1, -3, -1, 1]
+    g[:, :4] = np.array(gd["g"], np.float32)
     dbg = oracle.step(wl, theta, m, g, 1, debug=True)
-    assert dbg["codes"][0, :4].tolist() == [0, 0, 1, -1]
-    assert dbg["codes"][1, :4].tolist() == [1, -1, -1, 1]
-    assert dbg["sums"].tolist() == [1, -1, 0, 0]
-    assert dbg["sign"].tolist() == [1, -1, 0, 0]
+    assert dbg["codes"][:, :4].tolist() == gd["codes"]
+    assert dbg["sums"].tolist() == gd["sums"]
+    assert dbg["sign"].tolist() == gd["sign"]
     a = 1 - float(np.float32(1e-4)) * float(np.float32(0.1))
     np.testing.assert_allclose(theta[2:], a * th0[2:].astype(np.float64), rtol=1e-7)
     assert theta[0] < th0[0] - 9e-5 and theta[1] > th0[1] + 9e-5
@@ -470,11 +459,13 @@ def test_majority_tie_rate(oracle, W):
     m = rs.normal(0, 1e-3, (W, d)).astype(np.float32)
     g = (rs.standard_t(3, (W, d)) * 1e-3).astype(np.float32)
     dbg = oracle.step(wl, theta, m, g, 1, debug=True)
+    gd = golden("tie_rate.json")
     p = math.comb(W, W // 2) / 2**W
+    assert p == gd["closed_form"][str(W)]
     rate = float(np.mean(2 * dbg["counts"].astype(int) == W))
     assert abs(rate - p) < 5 * math.sqrt(p * (1 - p) / d)
     if W == 4:
-        assert rate > 0.30
+        assert rate > gd["W4_min_rate"]
 
 
 # ------------------------------------------------- streaming form ---------
@@ -562,17 +553,20 @@ def test_apply_closed_form(oracle):
 
 
 def test_pack_codes_handworked(oracle):
-    """n = 4: codes [1, -1, 7, -7, 0, 3] are the nibbles 1, F, 7, 9, 0, 3 from
-    the least significant end: word 0x003097F1.  n = 3: element 10 occupies
-    bits 30..32 and straddles words 0 and 1; code -3 is 0b101 (bits 30, 32)."""
-    c = np.zeros((1, 64), np.int8)
-    c[0, :6] = [1, -1, 7, -7, 0, 3]
-    w = oracle.pack_codes(c, 6, 4)
-    assert w.shape == (1, 8) and int(w[0, 0]) == 0x003097F1 and not w[0, 1:].any()
-    c = np.zeros((1, 64), np.int8)
-    c[0, 10] = -3
-    w = oracle.pack_codes(c, 11, 3)
-    assert int(w[0, 0]) == 1 << 30 and int(w[0, 1]) == 1 and not w[0, 2:].any()
+    """tests/golden/pack_codes_n4_n3.json: n = 4: codes [1, -1, 7, -7, 0, 3]
+    are the nibbles 1, F, 7, 9, 0, 3 from the least significant end: word
+    0x003097F1.  n = 3: element 10 occupies bits 30..32 and straddles words 0
+    and 1; code -3 is 0b101 (bits 30, 32)."""
+    for case in golden("pack_codes_n4_n3.json")["cases"]:
+        c = np.zeros((1, 64), np.int8)
+        for j, v in case["codes"].items():
+            c[0, int(j)] = v
+        w = oracle.pack_codes(c, case["d"], case["n"])
+        assert w.shape == (1, 2 * case["n"])
+        want = np.zeros(2 * case["n"], np.uint32)
+        for k, v in case["words"].items():
+            want[int(k)] = v
+        assert np.array_equal(w[0].view(np.uint32), want), case
 
 
 @pytest.mark.parametrize("n", [2, 3, 4, 5, 7, 8])
@@ -649,13 +643,13 @@ def test_stats_match_flip_handworked(oracle):
       w2 = [-3, 3, 3, 3]:             M1 = 3,    codes [-1, 1, 1, 1]
     sums [1, 3, 3, 1] -> signs all +1; sum of c [-2, 3.5, 3.5, 3] -> column 0
     flips, columns 1-3 match."""
-    wl = wls.flat("mf", 4, W=3, agg="l1", qbits=2, beta1=0.5)
+    gd = golden("stats_match_flip.json")
+    wl = wls.flat("mf", 4, W=gd["W"], agg="l1", qbits=gd["n"], beta1=gd["beta1"])
     g = np.zeros((3, 64), np.float32)
-    g[0, :4] = g[1, :4] = np.array([0.5, 0.25, 0.25, 0.0]) * 2
-    g[2, :4] = np.array([-3.0, 3.0, 3.0, 3.0]) * 2
+    g[:, :4] = np.array(gd["c"], np.float32) * 2           # c = g/2 with m = 0
     dbg = oracle.step(wl, np.zeros(4, np.float32), np.zeros((3, 64), np.float32), g, 1, debug=True)
-    assert dbg["sums"].tolist() == [1, 3, 3, 1]
-    assert dbg["stats"][0].tolist() == [0, 3, 1, 0]
+    assert dbg["sums"].tolist() == gd["sums"]
+    assert dbg["stats"][0].tolist() == gd["stats_ties_match_flip_zero"]
 
 
 def test_stats_momentum_variance_exact(oracle):
@@ -686,10 +680,10 @@ def test_stats_momentum_variance_exact(oracle):
 def test_splitmix64_published_outputs(oracle):
     """SplitMix64 (Steele, Lea, Flood 2014; Vigna's reference C version):
     the published first outputs for seeds 1234567 and 0."""
-    want = [6457827717110365317, 3203168211198807973, 9817491932198370423,
-            4593380528125082431, 16408922859458223821]
+    gd = golden("splitmix64.json")
+    want = [int(v) for v in gd["seed_1234567_first5"]]
     assert [oracle.splitmix64(1234567, k) for k in range(5)] == want
-    assert oracle.splitmix64(0, 0) == 0xE220A8397B1DCDAF
+    assert oracle.splitmix64(0, 0) == int(gd["seed_0_first"])
 
 
 def test_minf_is_numpy_max_abs(oracle):
@@ -803,18 +797,19 @@ def test_qinf_zeroes_most_heavy_tailed_updates(oracle):
     """The pages' finding (Lion Cub review, Figure 3 and Figure 4): on
     heavy-tailed update vectors the max-norm quantiser sends most entries to
     zero and matches few signs, while Eq. (1) keeps most signs."""
+    gd = golden("q_inf_heavy_tail.json")
     rs = np.random.default_rng(5)
     d = 1 << 18
-    wl = wls.flat("ht", d, W=1, agg="linf", qbits=4)
+    wl = wls.flat("ht", d, W=1, agg="linf", qbits=gd["n"])
     x = np.zeros((1, wl.ld), np.float32)
-    x[0, :d] = (rs.standard_t(2.5, d) * 1e-3).astype(np.float32)
+    x[0, :d] = (rs.standard_t(gd["student_t_nu"], d) * 1e-3).astype(np.float32)
     ci, _ = oracle.quant_linf(wl, x, 1)
     c1, _ = oracle.quant_l1(wl.with_(agg="l1"), x)
     zi, z1 = np.mean(ci[0, :d] == 0), np.mean(c1[0, :d] == 0)
     mi = np.mean(np.sign(ci[0, :d]) == np.sign(x[0, :d]))
     m1 = np.mean(np.sign(c1[0, :d]) == np.sign(x[0, :d]))
-    assert zi > 0.5 and z1 < 0.2
-    assert m1 > mi + 0.5
+    assert zi > gd["q_inf_zero_fraction_min"] and z1 < gd["l1_zero_fraction_max"]
+    assert m1 > mi + gd["l1_minus_q_inf_match_min"]
 
 
 def test_linf_step_equals_vote_when_magnitudes_are_equal(oracle):
