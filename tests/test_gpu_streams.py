@@ -108,3 +108,27 @@ def test_step_captured_in_a_graph_and_replayed(agg):
     del graph
     lc.close()
     le.close()
+
+
+def test_stream_probe_kernels():
+    """The measurement hook's reference kernels compute what they claim:
+    copy c = a, triad c = a + 0.5 b (0.5 b is exact, so one rounding)."""
+    import torch
+
+    from communication_compressed_distributed_amd import _abi
+    n = 3 * 4096
+    rs = np.random.default_rng(2)
+    a_h = rs.normal(0, 1, n).astype(np.float32)
+    b_h = rs.normal(0, 1, n).astype(np.float32)
+    a, b = to_dev(a_h), to_dev(b_h)
+    c = torch.full((n,), 7.0, device="cuda")
+    h = _abi._stream_handle()
+    _abi.lioncub_stream_probe(_abi.STREAM_READ, a, None, c, n, h)
+    torch.cuda.synchronize()
+    assert torch.all(c == 7.0)                 # the read kernel writes nothing
+    _abi.lioncub_stream_probe(_abi.STREAM_COPY, a, None, c, n, h)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(c), a_h)
+    _abi.lioncub_stream_probe(_abi.STREAM_TRIAD, a, b, c, n, h)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(c), a_h + np.float32(0.5) * b_h)
