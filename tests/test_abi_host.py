@@ -115,3 +115,13 @@ def test_stream_probe_rejects_bad_arguments_before_device():
     assert L.lioncub_stream_probe(0, p, p, p, 0, None) == _abi.EINVAL
     assert L.lioncub_stream_probe(2, p, None, p, 4096, None) == _abi.EINVAL     # triad needs b
     assert L.lioncub_stream_probe(1, C.c_void_p(260), p, p, 4096, None) == _abi.EALIGN
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    """No fallback: without the built library the product path raises."""
+    monkeypatch.setattr(_abi, "_lib", None)
+    monkeypatch.setattr(_abi, "LIB_PATH", str(tmp_path / "liblioncub.so"))
+    with pytest.raises(ImportError):
+        _abi.lib()
+    with pytest.raises(ImportError):
+        _abi.lioncub_workspace_bytes(cfg())
