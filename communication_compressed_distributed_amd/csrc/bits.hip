@@ -6,10 +6,11 @@
 // signs (D-Lion summary page, "Approach": majority vote).  These are the two
 // halves of the 1-bit exchange; the fused step does both in registers.
 //
-// Pack: each lane loads a 16-byte quad, forms a 4-bit nibble, and four wave
-// ballots give the 256 bits of the wave; the LSB-first 64-bit word of
-// elements 64k..64k+63 is assembled from bits 16k..16k+15 of the ballots by a
-// 4-way bit spread and stored by lane 16k.
+// Pack: each lane loads 16-byte quads and forms 4-bit nibbles; each row of
+// 16 lanes assembles the LSB-first 64-bit word of its 64 elements by a DPP
+// OR scan (row_pack_word), and the row's last lane stores it.  (Measured on
+// MI355X: two workers per workgroup, or the words staged in LDS and written
+// as one 512-byte run, were no faster.)
 //
 // Vote: each lane owns one 64-element word column and counts with bit-sliced
 // adders; see k_vote_sliced.  Besides counts and signs it can emit the
@@ -50,8 +51,8 @@ __global__ __launch_bounds__(kThreads) void k_pack(PackParams p) {
 #pragma unroll
       for (int k = 0; k < 4; ++k) nib |= (k < nv[q] ? sign_bit(x[q].v[k], p.parity) : 0u) << k;
     }
-    const uint64_t word = wave_pack_words(nib);
-    if ((tid & 15) == 0 && j < p.ld) p.bits[i * (p.ld >> 6) + (j >> 6)] = word;
+    const uint64_t word = row_pack_word(nib);
+    if ((tid & 15) == 15 && j < p.ld) p.bits[i * (p.ld >> 6) + (j >> 6)] = word;
   }
 }
 

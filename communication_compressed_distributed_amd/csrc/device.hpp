@@ -182,29 +182,27 @@ __device__ __forceinline__ uint32_t nibble_to_bytes(uint32_t nib) {
   return (nib * 0x00204081u) & 0x01010101u;
 }
 
-// Spread the 16 low bits of x so that bit i lands on bit 4*i (Morton-style
-// interleave by masks; "Bit Twiddling Hacks", S. E. Anderson, public domain).
-__device__ __forceinline__ uint64_t spread4(uint64_t x) {
-  x &= 0xFFFFull;
-  x = (x | (x << 24)) & 0x000000FF000000FFull;
-  x = (x | (x << 12)) & 0x000F000F000F000Full;
-  x = (x | (x << 6)) & 0x0303030303030303ull;
-  x = (x | (x << 3)) & 0x1111111111111111ull;
-  return x;
-}
-
 // Wave64 sign bitmap of the 256 consecutive elements held 4 per lane: lane l
-// holds bits nib (bit r = element 4l+r).  Returns, in lanes with l % 16 == 0,
-// the 64-bit word of elements 64*(l/16) .. +63 (LSB first).  Every lane of
-// the wave must call it (inactive lanes contribute zero bits).
-__device__ __forceinline__ uint64_t wave_pack_words(uint32_t nib) {
-  const uint64_t b0 = __ballot(nib & 1u);
-  const uint64_t b1 = __ballot(nib & 2u);
-  const uint64_t b2 = __ballot(nib & 4u);
-  const uint64_t b3 = __ballot(nib & 8u);
-  const int sh = 16 * ((threadIdx.x & 63) >> 4);
-  return spread4(b0 >> sh) | (spread4(b1 >> sh) << 1) | (spread4(b2 >> sh) << 2) |
-         (spread4(b3 >> sh) << 3);
+// holds bits nib (bit r = element 4l+r).  Each row of 16 lanes owns one
+// 64-bit word (elements 64*(l/16) .. +63, LSB first): lane l%16 = r places
+// its nibble at bit 4r of the low (r < 8) or high half, and an OR prefix scan
+// over the row with DPP row shifts by 1, 2, 4 and 8 lanes leaves the whole
+// word in lane r = 15.  Returns it there (partial ORs elsewhere).  Every lane
+// of the wave must call it, with all 64 lanes active.
+__device__ __forceinline__ uint64_t row_pack_word(uint32_t nib) {
+  const int r = threadIdx.x & 15;
+  uint32_t lo = r < 8 ? nib << (4 * r) : 0u;
+  uint32_t hi = r >= 8 ? nib << (4 * (r - 8)) : 0u;
+  // dpp_ctrl 0x110 + n = row_shr:n; lanes with no source in the row read 0
+  lo |= static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(lo), 0x111, 0xF, 0xF, true));
+  hi |= static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(hi), 0x111, 0xF, 0xF, true));
+  lo |= static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(lo), 0x112, 0xF, 0xF, true));
+  hi |= static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(hi), 0x112, 0xF, 0xF, true));
+  lo |= static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(lo), 0x114, 0xF, 0xF, true));
+  hi |= static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(hi), 0x114, 0xF, 0xF, true));
+  lo |= static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(lo), 0x118, 0xF, 0xF, true));
+  hi |= static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(hi), 0x118, 0xF, 0xF, true));
+  return (static_cast<uint64_t>(hi) << 32) | lo;
 }
 
 // Sign bit of one element: 1 for c > 0, 0 for c < 0, parity for an exact

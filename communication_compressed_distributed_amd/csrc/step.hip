@@ -243,8 +243,10 @@ __device__ __forceinline__ void step_block(const StepParams& p, const BlockEnt& 
         if (AGG == kAggVote || AGG == kAggAvg) {
           cnt[q] += nibble_to_bytes(nib);
           if (DBG && p.bits) {
-            const uint64_t word = wave_pack_words(nib);  // every lane takes part
-            if ((tid & 15) == 0 && (FULL || nv[q] > 0))
+            const uint64_t word = row_pack_word(nib);  // every lane takes part
+            // the row's last lane stores the word if its first element exists
+            // (in a ragged tail that lane itself may hold none)
+            if ((tid & 15) == 15 && (FULL || (j[q] & ~int64_t{63}) < be.start + be.len))
               p.bits[static_cast<int64_t>(i) * (p.ld >> 6) + (j[q] >> 6)] = word;
           }
         } else if (kQ && DBG && p.codes && (FULL || nv[q] > 0)) {
