@@ -16,7 +16,8 @@
  * W <= 5, exact rational arithmetic for Eq. (1) and for exactly summable
  * mean-|x| inputs, the summation error bound for the rest, invariants, and
  * torch's bf16 conversion.  The fixed order of the mean-|x| tree is a
- * definition of this project (the pages only say "mean absolute value"):
+ * definition of this project (the pages define M1 only as the mean of the
+ * absolute values, with no order of summation):
  * beyond the exact-sum cases and the error bound it is parity unpinned.
  */
 #include "lco.h"
