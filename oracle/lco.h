@@ -12,8 +12,8 @@
  *         pith.science review page: section "What carries the argument"
  *         (the pre-sign update vector c_{i,t}, the 0/1 sign packing with
  *         exact zeros alternated by iteration parity, Eq. (1) L1
- *         quantisation), "Core claim", the assumptions list ("alternating
- *         0 to +1 or -1 on odd and even iterations"), Figure 1 and
+ *         quantisation), "Core claim", the assumptions list (zeros sent as
+ *         +1 on odd and -1 on even iterations), Figure 1 and
  *         Figure 10 captions, and the reference-graph note that with 4
  *         workers over 30% of majority votes tie.
  *   [DL]  "Communication Efficient Distributed Training with Distributed
