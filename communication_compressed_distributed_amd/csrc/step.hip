@@ -21,10 +21,12 @@
 // stochastically against max |c|: the quantiser the Lion Cub page compares
 // Eq. (1) with (Figure 4).
 //
-// Workers are processed in batches of WB: all 2*WB loads of a batch are
-// issued before any use, which gives every wave 2*WB outstanding vector
-// loads; the batch's momentum stores follow.  HBM-bound: per element it moves
-// W*(4 + s_g + 4) + 2*s_theta bytes (vote) -- nothing else.
+// Workers are processed in batches of WB: the 2*WB*4 loads of a batch (m and
+// g of WB workers for the thread's 4 quads) are issued before any use, so
+// every lane keeps 16 vector loads in flight at WB = 2; the batch's momentum
+// stores follow.  HBM-bound: per element it moves W*(4 + s_g + 4) + 2*s_theta
+// bytes on every path -- nothing else (the quantised paths' norm pass is a
+// separate kernel).
 #include "device.hpp"
 #include "layout.hpp"
 
@@ -144,7 +146,7 @@ __device__ __forceinline__ void step_block(const StepParams& p, const BlockEnt& 
     if (FULL || nv[q] > 0) th[q] = ld_x4<TT>(p.theta, j[q], nv[q]);
 
   uint32_t cnt[Q];    // vote: per-element counts, one byte each
-  int sum[Q][4];      // L1: per-element integer sums
+  int sum[Q][4];      // quantised paths: per-element integer sums
   F4 acc[Q];          // averaging: running sum of new momenta
   // diagnostics (debug instantiations): unquantised sum of c in worker order,
   // fp64 sums of the new momenta and of their squares
@@ -165,7 +167,7 @@ __device__ __forceinline__ void step_block(const StepParams& p, const BlockEnt& 
     for (int k = 0; k < 4; ++k) sum[q][k] = 0;
   }
 
-  // The W scales of this tensor (L1 path) are staged in LDS once per block:
+  // The W scales of this tensor (quantised paths) are staged in LDS once per block:
   // a vector load after the batch's data loads would make every wave wait
   // for all of them before its first product; an LDS read is counted apart
   // from the memory loads and arrives first.
