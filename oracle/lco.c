@@ -376,6 +376,10 @@ void lco_step_range(const lco_cfg *cfg, int64_t j0, int64_t j1,
 
 /* ------------------------------------ max-norm stochastic baseline ---- */
 
+/* SplitMix64 (Steele, Lea and Flood, OOPSLA 2014): the generator adds the
+ * odd constant gamma to its state and mixes; as a counter-based generator
+ * output k of the stream seeded s is mix(s + (k+1)*gamma).  Pinned to the
+ * published first outputs. */
 uint64_t lco_splitmix64(uint64_t seed, uint64_t counter) {
   uint64_t z = seed + (counter + 1u) * 0x9E3779B97F4A7C15ull;
   z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
@@ -392,6 +396,14 @@ double lco_minf(const float *x, int64_t n) {
   return mx;
 }
 
+/* [LC] Figure 4 caption and the referee report on Eq. (1): the standard
+ * max-normalised quantiser with stochastic rounding, the baseline Eq. (1) is
+ * measured against; the pages name it but print no formula, so this is the
+ * reading of Eq. (1) with max |x| for M1 and stochastic rounding:
+ * floor(y) + [u < y - floor(y)], y = (2^(n-1)-1)/max|x| * x in fp64,
+ * u = (draw >> 11) * 2^-53, clamped.  PARITY PARTLY UNPINNED (the formula is
+ * a reading); pinned: integer y, the threshold's direction, the clamp,
+ * unbiasedness and the pages' zero-collapse finding. */
 int8_t lco_qinf(float c, double minf, int32_t qbits, uint64_t draw) {
   int32_t qmax = (1 << (qbits - 1)) - 1;
   if (minf == 0.0) return 0;
