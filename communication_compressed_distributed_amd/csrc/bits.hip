@@ -143,7 +143,33 @@ __global__ __launch_bounds__(kThreads) void k_vote_sliced(VoteParams p) {
       }
       sw[g] = s4;
     }
-    if (rem >= 64) {
+    // A workgroup whose 256 words all lie below d writes through LDS: each
+    // wave's 4 KB of counts (and of signs) is stored as 4 instructions of 64
+    // consecutive 16-byte pieces (lane l's 64 bytes are 4 pieces; the XOR
+    // swizzle spreads both the writes and the reads over the LDS banks).
+    // Every thread of such a workgroup is present (none returned above).
+    const int64_t wg_end = (static_cast<int64_t>(blockIdx.x) + 1) * kThreads;
+    if (wg_end <= p.words && (wg_end << 6) <= p.d) {
+      __shared__ uint4 sh[2][kThreads * 4];  // [counts, signs][16-byte piece]
+      const int lane = threadIdx.x & 63, wbase = (threadIdx.x >> 6) * 256;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int slot = wbase + 4 * lane + (q ^ (lane & 3));
+        sh[0][slot] = make_uint4(cw[4 * q], cw[4 * q + 1], cw[4 * q + 2], cw[4 * q + 3]);
+        sh[1][slot] = make_uint4(sw[4 * q], sw[4 * q + 1], sw[4 * q + 2], sw[4 * q + 3]);
+      }
+      __syncthreads();
+      // piece P = 64k + lane of the wave's chunk came from lane P/4, quad P%4
+      const int64_t wave_j0 = (static_cast<int64_t>(blockIdx.x) * kThreads + wbase / 4) << 6;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int src = 16 * k + (lane >> 2);
+        const int slot = wbase + 4 * src + ((lane & 3) ^ (src & 3));
+        const int64_t off = wave_j0 + 16 * (64 * k + lane);
+        if (p.counts) *reinterpret_cast<uint4*>(p.counts + off) = sh[0][slot];
+        if (p.sign) *reinterpret_cast<uint4*>(p.sign + off) = sh[1][slot];
+      }
+    } else if (rem >= 64) {
       if (p.counts) {
 #pragma unroll
         for (int q = 0; q < 4; ++q)

@@ -119,14 +119,16 @@ def test_pack_vote_handworked(t, tie):
     lc.close()
 
 
+@pytest.mark.parametrize("d", [3 * 4096 + 1001, 3 * 16384 + 1001, 4 * 16384])
 @pytest.mark.parametrize("W", [1, 2, 3, 4, 5, 8, 17])
 @pytest.mark.parametrize("t", [1, 2])
-def test_pack_vote_random(W, t):
+def test_pack_vote_random(W, t, d):
     """Ragged d, exact zeros, padded rows; bitwise against the oracle (whose
-    pack and vote are pinned by brute force and NumPy's packbits)."""
+    pack and vote are pinned by brute force and NumPy's packbits).  The
+    larger sizes span several full vote workgroups (256 words: the
+    LDS-staged store path) and a partial last one."""
     import torch
     rs = np.random.default_rng(W * 10 + t)
-    d = 3 * 4096 + 1001
     ld = (d + 63) // 64 * 64 + 128
     wl, lc = _ctx(W, d, ld=ld)
     x = rs.standard_normal((W, ld)).astype(np.float32)
@@ -139,6 +141,8 @@ def test_pack_vote_random(W, t):
     lc.vote(bits, t, counts, sign)
     only_sign = torch.zeros(d, dtype=torch.int8, device="cuda")
     lc.vote(bits, t, None, only_sign)
+    only_counts = torch.zeros(d, dtype=torch.uint8, device="cuda")
+    lc.vote(bits, t, only_counts, None)
     torch.cuda.synchronize()
     wb = lco.pack(x, d, t)
     assert np.array_equal(to_host(bits).view(np.uint64), wb)
@@ -146,6 +150,7 @@ def test_pack_vote_random(W, t):
     assert np.array_equal(to_host(counts), wc)
     assert np.array_equal(to_host(sign), ws)
     assert np.array_equal(to_host(only_sign), ws)
+    assert np.array_equal(to_host(only_counts), wc)
     lc.close()
 
 
