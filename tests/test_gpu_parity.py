@@ -381,15 +381,17 @@ def test_one_bit_path_composes_into_the_step(W):
     lc.close()
 
 
+@pytest.mark.parametrize("d", [4096 + 1000 + 7, 3 * 8192 + 1000 + 7, 4 * 8192])
 @pytest.mark.parametrize("n", [2, 3, 4, 5, 6, 7, 8])
 @pytest.mark.parametrize("W", [1, 3, 16])
-def test_wire_pack_and_unpack_sum(n, W):
+def test_wire_pack_and_unpack_sum(n, W, d):
+    """Sizes from one partial workgroup to several full unpack workgroups
+    (8192 elements each) and a partial last one; row padding past d."""
     import torch
     qmax = 2 ** (n - 1) - 1
     rs = np.random.default_rng(10 * n + W)
-    d = 4096 + 1000 + 7
-    ld = (d + 63) // 64 * 64
-    wl, lc = _ctx(W, d, agg="l1", qbits=n)
+    ld = (d + 63) // 64 * 64 + 64
+    wl, lc = _ctx(W, d, ld=ld, agg="l1", qbits=n)
     codes = rs.integers(-qmax, qmax + 1, (W, ld)).astype(np.int8)   # junk past d too
     wire = torch.full((W, (ld // 32) * n), -1, dtype=torch.int32, device="cuda")
     lc.pack_codes(to_dev(codes), wire)
@@ -398,6 +400,8 @@ def test_wire_pack_and_unpack_sum(n, W):
     lc.unpack_sum(wire, sums, sign)
     only_sign = torch.zeros(d, dtype=torch.int8, device="cuda")
     lc.unpack_sum(wire, None, only_sign)
+    only_sums = torch.zeros(d, dtype=torch.int32, device="cuda")
+    lc.unpack_sum(wire, only_sums, None)
     torch.cuda.synchronize()
     ww = lco.pack_codes(codes, d, n)
     assert np.array_equal(to_host(wire).view(np.uint32), ww)
@@ -405,6 +409,7 @@ def test_wire_pack_and_unpack_sum(n, W):
     assert np.array_equal(to_host(sums), ws)
     assert np.array_equal(to_host(sign), wsg)
     assert np.array_equal(to_host(only_sign), wsg)
+    assert np.array_equal(to_host(only_sums), ws)
     lc.close()
 
 
