@@ -92,7 +92,50 @@ __global__ __launch_bounds__(kThreads) void k_unpack_sum(WireParams p) {
     }
   }
   const int64_t valid = p.d - j0;
-  if (valid >= 32) {
+  // A workgroup whose 256 groups all lie below d writes through LDS: each
+  // wave's 8 KB of sums (and 2 KB of signs) is stored as instructions of 64
+  // consecutive 16-byte pieces instead of pieces 128 (32) bytes apart; the
+  // XOR swizzles spread the LDS writes and reads over the banks (measured
+  // about 5% faster).  Every thread of such a workgroup is present (none
+  // returned above).
+  const int64_t wg_end = (static_cast<int64_t>(blockIdx.x) + 1) * kThreads * 32;
+  if (wg_end <= p.d) {
+    __shared__ int4 sh_s[kThreads * 8];
+    __shared__ uint4 sh_g[kThreads * 2];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    uint32_t sg[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) sg[k] = 0;
+#pragma unroll
+    for (int k = 0; k < 32; ++k)
+      sg[k >> 2] |= (static_cast<uint32_t>((S[k] > 0) - (S[k] < 0)) & 0xFFu) << (8 * (k & 3));
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      sh_s[wave * 512 + 8 * lane + (q ^ (lane & 7))] =
+          make_int4(S[4 * q], S[4 * q + 1], S[4 * q + 2], S[4 * q + 3]);
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+      sh_g[wave * 128 + 2 * lane + (q ^ (lane & 1))] =
+          make_uint4(sg[4 * q], sg[4 * q + 1], sg[4 * q + 2], sg[4 * q + 3]);
+    __syncthreads();
+    const int64_t wave_j0 = (static_cast<int64_t>(blockIdx.x) * kThreads + 64 * wave) << 5;
+    if (p.sums) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {  // piece 64k + lane: lane src's quad lane % 8
+        const int src = 8 * k + (lane >> 3);
+        *reinterpret_cast<int4*>(p.sums + wave_j0 + 4 * (64 * k + lane)) =
+            sh_s[wave * 512 + 8 * src + ((lane & 7) ^ (src & 7))];
+      }
+    }
+    if (p.sign) {
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int src = 32 * k + (lane >> 1);
+        *reinterpret_cast<uint4*>(p.sign + wave_j0 + 16 * (64 * k + lane)) =
+            sh_g[wave * 128 + 2 * src + ((lane & 1) ^ (src & 1))];
+      }
+    }
+  } else if (valid >= 32) {
     if (p.sums) {
 #pragma unroll
       for (int k = 0; k < 32; k += 4)
