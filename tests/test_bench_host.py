@@ -40,3 +40,28 @@ def test_gpus_above_one_exit_with_a_message(capsys):
         sys.argv = argv
     assert e.value.code == 2
     assert "one GPU" in capsys.readouterr().err
+
+
+@pytest.mark.parametrize("name,step_total,fused,norm", [
+    ("flat-1M-w4-vote", 56, 56, 0),                          # 4*(4+4+4) + 2*4
+    ("gpt2-124M-w8-vote", 104, 104, 0),                      # 8*12 + 8
+    ("flat-350M-w16-l1q4", 328, 200, 128),                   # 16*8 + (16*12 + 8)
+    ("gpt-760M-w8-vote-bf16-syncemb", 84, 84, 0),            # 8*(4+2+4) + 2*2
+    ("gpt-1.3B-w8-l1q8-bf16g", 136, 88, 48),                 # 8*6 + (8*10 + 8)
+])
+def test_algorithmic_bytes_per_parameter(name, step_total, fused, norm):
+    """The roofline's numerator: what the method must move per parameter
+    with every intermediate in registers (m and g read and m written once
+    per worker, theta read and written once; the quantised paths read m and
+    g once more for the norm pass)."""
+    wl = wls.BY_NAME[name]
+    b = bench.bytes_per_param(wl)
+    assert b["step_total"] == step_total
+    kind = {"vote": "vote_step", "l1": "l1_step"}[wl.agg]
+    assert b[kind] == fused
+    assert (b["m1_partial"] if wl.agg == "l1" else 0) == norm
+    # the whole step's bytes at the workload's size (GB), as the bench prices it
+    assert abs(step_total * wl.d / 1e9 - {"flat-1M-w4-vote": 0.0587, "gpt2-124M-w8-vote": 12.94,
+                                         "flat-350M-w16-l1q4": 114.8,
+                                         "gpt-760M-w8-vote-bf16-syncemb": 63.73,
+                                         "gpt-1.3B-w8-l1q8-bf16g": 178.65}[name]) < 0.01
