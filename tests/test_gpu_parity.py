@@ -566,3 +566,15 @@ def test_tiny_vectors(agg, d, W):
     wl = wls.flat("tiny", d, W=W, agg=agg, qbits=0 if agg in ("vote", "avg") else 4)
     gpu_step_vs_oracle(wl, steps=3, debug=True)
     gpu_step_vs_oracle(wl, steps=1, debug=False, seed_shift=1)
+
+
+@pytest.mark.parametrize("agg", ["vote", "l1", "linf"])
+def test_sync_every_ten_over_twelve_steps(agg):
+    """The pages' interval: momentum of the embedding tensors averaged every
+    10 steps.  Twelve consecutive steps from t = 1, compared after each, so
+    step 10 averages and steps 1-9, 11, 12 do not."""
+    wl = wls.Workload(name="s10", tensors=[("wte", 2 * 4096 + 64), ("h", 4096 + 128),
+                                           ("wpe", 128)], W=4, agg=agg,
+                      qbits=0 if agg == "vote" else 4, sync_names=("wte", "wpe"), sync_every=10,
+                      theta_dtype="bf16", grad_dtype="bf16")
+    gpu_step_vs_oracle(wl, steps=12, t0=1, debug=True)
