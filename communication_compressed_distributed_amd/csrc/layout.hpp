@@ -73,8 +73,12 @@ struct StepParams {
   uint8_t* counts;
   int32_t* sums;
   int8_t* sign;
-  // diagnostics: per-block partials [nblk][kStat] (workspace), then per tensor
+  // diagnostics: per-block partials [nblk][kStat] and per-group partials
+  // [ngrp][kStat] (workspace), then per tensor
   uint64_t* bstat;
+  uint64_t* gstat;
+  const GroupEnt* grp;  // groups of kGroup consecutive blocks of one tensor
+  int32_t ngrp;
   uint64_t* stats;     // [nT][4]: ties, sign matches, flips, zero signs
   double* mvar_max;    // [nT]: largest inter-worker variance of the new momenta
 };

@@ -44,7 +44,7 @@ namespace {
 constexpr size_t kWsAlign = 256;
 
 struct WsLayout {
-  size_t blk, tens, grp, partial, gval, m1, scale, bstat, total;
+  size_t blk, tens, grp, partial, gval, m1, scale, bstat, gstat, total;
 };
 
 size_t align_up(size_t x) { return (x + kWsAlign - 1) / kWsAlign * kWsAlign; }
@@ -68,6 +68,8 @@ WsLayout ws_layout(int64_t nblk, int64_t ngrp, int64_t nT, int64_t W) {
   o = align_up(o + static_cast<size_t>(W * nT) * sizeof(double));
   L.bstat = o;
   o = align_up(o + static_cast<size_t>(nblk) * kStat * sizeof(uint64_t));
+  L.gstat = o;
+  o = align_up(o + static_cast<size_t>(ngrp) * kStat * sizeof(uint64_t));
   L.total = o;
   return L;
 }
@@ -127,6 +129,7 @@ struct lioncub_ctx {
   double* m1;
   double* scale;
   uint64_t* bstat;
+  uint64_t* gstat;
   std::vector<BlockEnt> h_blk;
   std::vector<TensorEnt> h_tens;
   std::vector<GroupEnt> h_grp;
@@ -161,6 +164,9 @@ void fill_step_params(const lioncub_ctx* c, StepParams* p) {
   p->tens = c->tens;
   p->scale = c->scale;
   p->bstat = c->bstat;
+  p->gstat = c->gstat;
+  p->grp = c->grp;
+  p->ngrp = c->ngrp;
   p->ld = c->cfg.ld;
   p->W = c->cfg.W;
   p->nT = c->cfg.n_tensors;
@@ -237,6 +243,7 @@ int lioncub_init(lioncub_ctx** out, const lioncub_config* cfg, void* hip_stream,
   c->m1 = reinterpret_cast<double*>(ws + L.m1);
   c->scale = reinterpret_cast<double*>(ws + L.scale);
   c->bstat = reinterpret_cast<uint64_t*>(ws + L.bstat);
+  c->gstat = reinterpret_cast<uint64_t*>(ws + L.gstat);
 
   c->h_tens.resize(cfg->n_tensors);
   c->h_blk.reserve(nblk);

@@ -68,41 +68,80 @@ __device__ __forceinline__ void block_stats(const StepParams& p, unsigned tie, u
   }
 }
 
-// One workgroup per tensor: fold its blocks' diagnostic slots.
+// Fold 256 (count, count, count, count, max) slots held one per thread:
+// thread 0 returns the workgroup's totals.  Integer sums and maxima are exact
+// in any order.
+__device__ __forceinline__ void fold_stats(uint64_t (&c)[4], double& v) {
+  __shared__ uint64_t sh_c[4][4];
+  __shared__ double sh_v[4];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int s = 32; s >= 1; s >>= 1) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) c[k] += __shfl_xor(c[k], s, kWave);
+    v = fmax(v, __shfl_xor(v, s, kWave));
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) sh_c[wave][k] = c[k];
+    sh_v[wave] = v;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) c[k] = (sh_c[0][k] + sh_c[1][k]) + (sh_c[2][k] + sh_c[3][k]);
+    v = fmax(fmax(sh_v[0], sh_v[1]), fmax(sh_v[2], sh_v[3]));
+  }
+}
+
+// Level 1: one workgroup per group of up to 256 consecutive blocks of one
+// tensor (the same group table as the mean-|c| finalize); thread l takes
+// block l's slots.
+__global__ __launch_bounds__(kThreads) void k_stats_group(StepParams p) {
+  const GroupEnt ge = p.grp[blockIdx.x];
+  uint64_t c[4] = {0, 0, 0, 0};
+  double v = 0.0;
+  if (static_cast<int>(threadIdx.x) < ge.cnt) {
+    const uint64_t* in = p.bstat + static_cast<int64_t>(ge.blk + threadIdx.x) * kStat;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) c[k] = in[k];
+    v = __longlong_as_double(static_cast<long long>(in[4]));
+  }
+  fold_stats(c, v);
+  if (threadIdx.x == 0) {
+    uint64_t* out = p.gstat + static_cast<int64_t>(blockIdx.x) * kStat;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) out[k] = c[k];
+    out[4] = static_cast<uint64_t>(__double_as_longlong(v));
+  }
+}
+
+// Level 2: one workgroup per tensor over its groups' slots.
 __global__ __launch_bounds__(kThreads) void k_stats_reduce(StepParams p) {
-  __shared__ uint64_t sh_c[kThreads][4];
-  __shared__ double sh_v[kThreads];
-  const int T = blockIdx.x, tid = threadIdx.x;
+  const int T = blockIdx.x;
   const TensorEnt te = p.tens[T];
   uint64_t c[4] = {0, 0, 0, 0};
   double v = 0.0;
-  for (int b = te.blk0 + tid; b < te.blk0 + te.nblk; b += kThreads) {
-    const uint64_t* in = p.bstat + static_cast<int64_t>(b) * kStat;
+  for (int g = te.grp0 + static_cast<int>(threadIdx.x); g < te.grp0 + te.ngrp; g += kThreads) {
+    const uint64_t* in = p.gstat + static_cast<int64_t>(g) * kStat;
 #pragma unroll
     for (int k = 0; k < 4; ++k) c[k] += in[k];
     v = fmax(v, __longlong_as_double(static_cast<long long>(in[4])));
   }
-#pragma unroll
-  for (int k = 0; k < 4; ++k) sh_c[tid][k] = c[k];
-  sh_v[tid] = v;
-  __syncthreads();
-  if (tid == 0) {
-    uint64_t tot[4] = {0, 0, 0, 0};
-    double mx = 0.0;
-    for (int u = 0; u < kThreads; ++u) {
-#pragma unroll
-      for (int k = 0; k < 4; ++k) tot[k] += sh_c[u][k];
-      mx = fmax(mx, sh_v[u]);
-    }
+  fold_stats(c, v);
+  if (threadIdx.x == 0) {
     if (p.stats) {
 #pragma unroll
-      for (int k = 0; k < 4; ++k) p.stats[static_cast<int64_t>(T) * 4 + k] = tot[k];
+      for (int k = 0; k < 4; ++k) p.stats[static_cast<int64_t>(T) * 4 + k] = c[k];
     }
-    if (p.mvar_max) p.mvar_max[T] = mx;
+    if (p.mvar_max) p.mvar_max[T] = v;
   }
 }
 
 hipError_t launch_stats_reduce(const StepParams& p, int nT, hipStream_t st) {
+  hipLaunchKernelGGL(k_stats_group, dim3(p.ngrp), dim3(kThreads), 0, st, p);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_stats_reduce, dim3(nT), dim3(kThreads), 0, st, p);
   return hipGetLastError();
 }

@@ -51,8 +51,10 @@ def test_workspace_bytes_layout():
     gval = 4 * 2 * 8
     m1 = 4 * 2 * 8
     bstat = 3 * 8 * 8
+    gstat = 2 * 8 * 8
     al = lambda x: (x + 255) // 256 * 256
-    assert n == al(blk) + al(tens) + al(grp) + al(part) + al(gval) + 2 * al(m1) + al(bstat)
+    assert n == (al(blk) + al(tens) + al(grp) + al(part) + al(gval) + 2 * al(m1) + al(bstat)
+                 + al(gstat))
     big = cfg(d=1_313_626_112, ld=1_313_626_112, W=8,
               tensor_offsets=[0, 1_000_000_000 // 64 * 64, 1_313_626_112])
     assert _abi.lioncub_workspace_bytes(big) > 0
