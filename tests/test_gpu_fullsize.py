@@ -145,3 +145,14 @@ def test_gpt_1B3_w8_l1q8_bf16g_fullsize():
     pick = [k for k, nm in enumerate(names)
             if nm in ("wte", "wpe", "ln_f.w", "ln_f.b") or nm.startswith(("h0.", "h23."))]
     run_fullsize(wl, steps=[1, 2], tensors=pick, n_random=1)
+
+
+@pytest.mark.parametrize("agg", ["vote", "l1"])
+def test_beyond_two_to_the_31_elements(agg):
+    """A vector of 2^31 + 4160 elements (2 workers): every element index,
+    block index and word index past 2^31 must be 64-bit; the samples include
+    the ragged end, and on the L1 path M1 of both rows is recomputed on the
+    host and compared bit for bit."""
+    wl = wls.flat(f"flat-2G-w2-{agg}", 2**31 + 4160, W=2, agg=agg, qbits=4 if agg == "l1" else 0,
+                  g_nu=3.0)
+    run_fullsize(wl, steps=[1], n_random=2)
