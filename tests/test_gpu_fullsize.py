@@ -156,3 +156,36 @@ def test_beyond_two_to_the_31_elements(agg):
     wl = wls.flat(f"flat-2G-w2-{agg}", 2**31 + 4160, W=2, agg=agg, qbits=4 if agg == "l1" else 0,
                   g_nu=3.0)
     run_fullsize(wl, steps=[1], n_random=2)
+
+
+def test_pack_and_vote_beyond_two_to_the_31_elements():
+    """lioncub_pack and lioncub_vote_bits on 3 rows of 2^31 + 4160 elements:
+    sampled word ranges (first, around 2^31, last) against the oracle."""
+    import torch
+    torch.cuda.set_device(0)
+    wl = wls.flat("flat-2G-w3-pack", 2**31 + 4160, W=3)
+    lc = lioncub_for(wl)
+    x = gen.device_m(wl)                          # any fp32 rows stand in for c
+    x[:, ::4099] = 0.0                            # exact zeros: the parity rule
+    words = wl.ld // 64
+    bits = torch.empty((wl.W, words), dtype=torch.int64, device="cuda")
+    sign_p = torch.empty(words, dtype=torch.int64, device="cuda")
+    zero_p = torch.empty(words, dtype=torch.int64, device="cuda")   # 16-byte aligned each
+    t = 3
+    lc.pack(x, t, bits)
+    lc.vote_bits(bits, t, sign_p, zero_p)
+    torch.cuda.synchronize()
+    for w0 in (0, (2**31 // 64) - 512, words - 1024):
+        w1 = min(words, w0 + 1024)
+        j0, j1 = 64 * w0, min(wl.d, 64 * w1)
+        xs = np.zeros((wl.W, 64 * (w1 - w0)), np.float32)
+        xs[:, : j1 - j0] = to_host(x[:, j0:j1])
+        want = lco.pack(xs, j1 - j0, t)
+        got = to_host(bits[:, w0:w1]).view(np.uint64)
+        assert np.array_equal(got, want), (w0, w1)
+        sb, zb = lco.vote_bits(want, wl.W, j1 - j0, t)
+        assert np.array_equal(to_host(sign_p[w0:w1]).view(np.uint64), sb), (w0, w1)
+        _say("pack/vote_bits words", w0, w1, "ok")
+    lc.close()
+    del x, bits, sign_p, zero_p
+    torch.cuda.empty_cache()
