@@ -132,3 +132,46 @@ def test_stream_probe_kernels():
     _abi.lioncub_stream_probe(_abi.STREAM_TRIAD, a, b, c, n, h)
     torch.cuda.synchronize()
     assert np.array_equal(to_host(c), a_h + np.float32(0.5) * b_h)
+
+
+def test_two_contexts_from_two_host_threads():
+    """The library keeps no global state: two host threads, each with its own
+    context and stream, step concurrently (ctypes releases the GIL during
+    the calls); both results equal the oracle's."""
+    import threading
+
+    import torch
+    wls_ = [wls.flat("ta", 3 * 4096 + 192, W=8, agg="l1", qbits=4),
+            wls.flat("tb", 5 * 4096 + 64, W=5, agg="vote", tie="zero", grad_dtype="bf16")]
+    results = [None, None]
+    errors = []
+
+    def worker(k):
+        try:
+            wl = wls_[k]
+            torch.cuda.set_device(0)
+            s = torch.cuda.Stream()
+            theta, m = _host_state(wl)
+            gs = [gen.host_g(wl, t) for t in (1, 2, 3, 4)]
+            with torch.cuda.stream(s):
+                lc = lioncub_for(wl, stream=s)
+                d_theta, d_m = to_dev(theta), to_dev(m)
+                d_gs = [to_dev(g, wl.grad_dtype == "bf16") for g in gs]
+                for t in (1, 2, 3, 4):
+                    lc.step(d_theta, d_m, d_gs[t - 1], t)
+            s.synchronize()
+            for t in (1, 2, 3, 4):
+                lco.step(wl, theta, m, gs[t - 1], t)
+            results[k] = (wl, d_theta, d_m, theta, m)
+            lc.close()
+        except Exception as e:  # reported below
+            errors.append(repr(e))
+
+    th = [threading.Thread(target=worker, args=(k,)) for k in (0, 1)]
+    for x in th:
+        x.start()
+    for x in th:
+        x.join()
+    assert not errors, errors
+    for wl, d_theta, d_m, theta, m in results:
+        _check(wl, d_theta, d_m, theta, m, f"thread {wl.name}")
