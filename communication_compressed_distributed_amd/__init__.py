@@ -46,6 +46,7 @@ class LionCub:
             tie_mode=TIE_ZERO if tie == "zero" else TIE_PARITY,
             beta1=beta1, beta2=beta2, lr=lr, wd=wd, sr_seed=sr_seed)
         self.d, self.ld, self.W, self.n_tensors = d, ld, W, len(offs) - 1
+        self.agg, self.sync_every = agg, sync_every
         self.spec = _checks.Spec(d=d, ld=ld, W=W, n_tensors=len(offs) - 1,
                                  theta_dtype=theta_dtype, grad_dtype=grad_dtype, qbits=qbits)
         nbytes = lioncub_workspace_bytes(self.cfg)
@@ -68,6 +69,39 @@ class LionCub:
     def step(self, theta, m, g, t, debug=None):
         _checks.step(self.spec, self.device, theta, m, g, debug)
         lioncub_step(self.ctx, theta, m, g, t, debug)
+
+    def capture(self, theta, m, gs, t0):
+        """Capture len(gs) consecutive steps (step t0 + k reads gs[k]) into a
+        torch.cuda.CUDAGraph and return it; graph.replay() runs them.
+
+        A step depends on t only through t's parity (zeros and ties) and
+        t % sync_every (averaging steps), so when K = len(gs) is a multiple
+        of lcm(2, sync_every), replaying the window is exactly the next K
+        steps: replay r runs steps t0 + r*K .. t0 + r*K + K - 1.  The
+        max-norm baseline draws its random numbers from the full t and is
+        refused.  The graph keeps the tensors it was captured with; the
+        caller refills gs between replays.  Profiling must be off."""
+        import math
+
+        import torch
+        K = len(gs)
+        period = 2 * self.sync_every // math.gcd(2, self.sync_every)
+        if self.agg == "linf":
+            raise ValueError("capture: the max-norm baseline's draws depend on the full step index")
+        if K == 0 or K % period:
+            raise ValueError(f"capture: the number of steps must be a multiple of {period}")
+        for g in gs:
+            _checks.state(self.spec, self.device, theta, m, g)
+        graph = torch.cuda.CUDAGraph()
+        prev = self.stream
+        try:
+            with torch.cuda.graph(graph):
+                self.set_stream(torch.cuda.current_stream())
+                for k, g in enumerate(gs):
+                    lioncub_step(self.ctx, theta, m, g, t0 + k, None)
+        finally:
+            self.set_stream(prev)
+        return graph
 
     def pack(self, x, t, bits):
         _checks.pack(self.spec, self.device, x, bits)

@@ -175,3 +175,52 @@ def test_two_contexts_from_two_host_threads():
     assert not errors, errors
     for wl, d_theta, d_m, theta, m in results:
         _check(wl, d_theta, d_m, theta, m, f"thread {wl.name}")
+
+
+@pytest.mark.parametrize("agg,sync_every,K", [("vote", 1, 2), ("l1", 3, 6), ("avg", 2, 4)])
+def test_captured_window_replays_as_the_next_steps(agg, sync_every, K):
+    """LionCub.capture: a window of K steps (K a multiple of lcm(2,
+    sync_every)) replayed three times equals 3K consecutive eager steps of
+    the oracle, with the gradients refilled between replays."""
+    import torch
+    wl = wls.Workload(name="cw", tensors=[("a", 2 * 4096 + 192), ("b", 4096 + 64)], W=4,
+                      agg=agg, qbits=4 if agg == "l1" else 0, sync_names=("b",),
+                      sync_every=sync_every)
+    theta, m = _host_state(wl)
+    d_theta, d_m = to_dev(theta), to_dev(m)
+    d_gs = [torch.empty((wl.W, wl.ld), device="cuda") for _ in range(K)]
+    lc = lioncub_for(wl)
+    t0 = 5
+    graph = lc.capture(d_theta, d_m, d_gs, t0)
+    torch.cuda.synchronize()
+    _check(wl, d_theta, d_m, theta, m, "after capture (nothing ran)")
+    t = t0
+    for rep in range(3):
+        gs = [gen.host_g(wl, t + k) for k in range(K)]
+        for k in range(K):
+            d_gs[k].copy_(to_dev(gs[k]))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for k in range(K):
+            lco.step(wl, theta, m, gs[k], t + k)
+        _check(wl, d_theta, d_m, theta, m, f"replay {rep}")
+        t += K
+    del graph
+    lc.close()
+
+
+def test_capture_refuses_windows_that_would_not_replay_exactly():
+    import torch
+    wl = wls.flat("cr", 4096, W=2, agg="vote", sync_every=3)
+    lc = lioncub_for(wl)
+    th, m = to_dev(_host_state(wl)[0]), to_dev(_host_state(wl)[1])
+    gs = [torch.zeros((2, wl.ld), device="cuda") for _ in range(4)]
+    with pytest.raises(ValueError):
+        lc.capture(th, m, gs, 1)                    # 4 is not a multiple of lcm(2, 3) = 6
+    lc.close()
+    wi = wls.flat("ci", 4096, W=2, agg="linf", qbits=4)
+    li = lioncub_for(wi)
+    with pytest.raises(ValueError):
+        li.capture(th, m, gs[:2], 1)                # max-norm draws depend on the full t
+    li.close()
