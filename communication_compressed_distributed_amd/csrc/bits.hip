@@ -8,9 +8,12 @@
 //
 // Pack: each lane loads 16-byte quads and forms 4-bit nibbles; each row of
 // 16 lanes assembles the LSB-first 64-bit word of its 64 elements by a DPP
-// OR scan (row_pack_word), and the row's last lane stores it.  (Measured on
-// MI355X: two workers per workgroup, or the words staged in LDS and written
-// as one 512-byte run, were no faster.)
+// OR scan (row_pack_word), and the row's last lane puts it in LDS; the first
+// wave then writes the workgroup's 64 words as one 512-byte run with
+// nontemporal stores.  (Measured on MI355X, 350M x 16: 3.75 ms against 4.3
+// with plain stores from the rows' last lanes, and 3.1 ms for the loads
+// alone; two workers per workgroup, or several blocks per workgroup, were
+// slower.)
 //
 // Vote: each lane owns one 64-element word column and counts with bit-sliced
 // adders; see k_vote_sliced.  Besides counts and signs it can emit the
@@ -30,6 +33,7 @@ struct PackParams {
 // grid: (ceil(ld/4096), W); 256 threads; 4096 elements (64 words) per
 // workgroup, 4 quads per thread (streaming 16-byte loads issued together).
 __global__ __launch_bounds__(kThreads) void k_pack(PackParams p) {
+  __shared__ uint64_t sh[kBlock / 64];
   const int tid = threadIdx.x;
   const int64_t i = blockIdx.y;
   const int64_t base = static_cast<int64_t>(blockIdx.x) * kBlock;
@@ -52,7 +56,12 @@ __global__ __launch_bounds__(kThreads) void k_pack(PackParams p) {
       for (int k = 0; k < 4; ++k) nib |= (k < nv[q] ? sign_bit(x[q].v[k], p.parity) : 0u) << k;
     }
     const uint64_t word = row_pack_word(nib);
-    if ((tid & 15) == 15 && j < p.ld) p.bits[i * (p.ld >> 6) + (j >> 6)] = word;
+    if ((tid & 15) == 15) sh[(j - base) >> 6] = word;  // word 16q + tid/16
+  }
+  __syncthreads();
+  if (tid < kBlock / 64) {
+    const int64_t j = base + 64 * tid;
+    if (j < p.ld) stnt_u64(p.bits + i * (p.ld >> 6) + (j >> 6), sh[tid]);
   }
 }
 
@@ -122,8 +131,8 @@ __global__ __launch_bounds__(kThreads) void k_vote_sliced(VoteParams p) {
     }
     const uint64_t tie = (p.W & 1) ? 0ull : eq;
     const uint64_t pos = gt | ((!p.tie_zero && p.parity) ? tie : 0ull);
-    p.sign_bits[wi] = pos & live;
-    if (p.zero_bits) p.zero_bits[wi] = (p.tie_zero ? tie : 0ull) & live;
+    stnt_u64(p.sign_bits + wi, pos & live);
+    if (p.zero_bits) stnt_u64(p.zero_bits + wi, (p.tie_zero ? tie : 0ull) & live);
   }
   if (p.counts || p.sign) {
     uint32_t cw[16], sw[16];
@@ -166,21 +175,21 @@ __global__ __launch_bounds__(kThreads) void k_vote_sliced(VoteParams p) {
         const int src = 16 * k + (lane >> 2);
         const int slot = wbase + 4 * src + ((lane & 3) ^ (src & 3));
         const int64_t off = wave_j0 + 16 * (64 * k + lane);
-        if (p.counts) *reinterpret_cast<uint4*>(p.counts + off) = sh[0][slot];
-        if (p.sign) *reinterpret_cast<uint4*>(p.sign + off) = sh[1][slot];
+        if (p.counts) stnt_u128(p.counts + off, sh[0][slot]);
+        if (p.sign) stnt_u128(p.sign + off, sh[1][slot]);
       }
     } else if (rem >= 64) {
       if (p.counts) {
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-          *reinterpret_cast<uint4*>(p.counts + j0 + 16 * q) =
-              make_uint4(cw[4 * q], cw[4 * q + 1], cw[4 * q + 2], cw[4 * q + 3]);
+          stnt_u128(p.counts + j0 + 16 * q,
+                    make_uint4(cw[4 * q], cw[4 * q + 1], cw[4 * q + 2], cw[4 * q + 3]));
       }
       if (p.sign) {
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-          *reinterpret_cast<uint4*>(p.sign + j0 + 16 * q) =
-              make_uint4(sw[4 * q], sw[4 * q + 1], sw[4 * q + 2], sw[4 * q + 3]);
+          stnt_u128(p.sign + j0 + 16 * q,
+                    make_uint4(sw[4 * q], sw[4 * q + 1], sw[4 * q + 2], sw[4 * q + 3]));
       }
     } else {
       for (int e = 0; e < rem; ++e) {

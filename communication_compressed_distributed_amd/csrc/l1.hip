@@ -246,10 +246,47 @@ __global__ __launch_bounds__(kThreads) void k_m1_finalize(M1Params p) {
   }
 }
 
-// Eq. (1) codes of x (or, MX, the stochastic max-norm codes): one
-// workgroup per block, all workers.
-template <bool MX>
+// Eq. (1) codes of x: one workgroup per (block, worker), grid (nblk, W);
+// the thread's four quads are loaded before any code is formed, and the
+// codes leave through nontemporal stores.  (Measured on MI355X, 350M x 16:
+// 4.6 ms, against 4.9 ms for one workgroup per block walking the workers.)
 __global__ __launch_bounds__(kThreads) void k_quant_codes(M1Params p, int8_t* __restrict__ codes) {
+  const BlockEnt be = block_of(p.blk, p.flat, p.d);
+  const int tid = threadIdx.x;
+  const int i = blockIdx.y;
+  const double qm = static_cast<double>(p.qmax);
+  const double s = p.scale[static_cast<int64_t>(i) * p.nT + be.tensor];
+  const int64_t row = static_cast<int64_t>(i) * p.ld + be.start;
+  F4 x[kRounds];
+  int nv[kRounds];
+#pragma unroll
+  for (int r = 0; r < kRounds; ++r) {
+    const int loc = kThreads * kQuad * r + kQuad * tid;
+    nv[r] = max(0, min(kQuad, be.len - loc));
+    if (nv[r] == kQuad) x[r] = ldnt_f32x4(p.x + row + loc, kQuad);
+    else x[r] = ldm_f32x4(p.x + row + loc, nv[r]);
+  }
+#pragma unroll
+  for (int r = 0; r < kRounds; ++r) {
+    if (nv[r] == 0) continue;
+    const int loc = kThreads * kQuad * r + kQuad * tid;
+    uint32_t packed = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      double y = __builtin_rint(static_cast<double>(x[r].v[k]) * s);
+      y = fmin(fmax(y, -qm), qm);
+      packed |= (static_cast<uint32_t>(static_cast<int>(y)) & 0xFFu) << (8 * k);
+    }
+    stnt_b4(codes + row + loc, packed, nv[r]);
+  }
+}
+
+// Stochastic max-norm codes: one workgroup per block walking all workers,
+// quad by quad.  This kernel is bound by the generator's 64-bit arithmetic,
+// not by HBM, and the long-lived workgroups keep the loads of the next quads
+// in flight behind it (the one-worker-per-workgroup form of the L1 kernel
+// above measured 7.0 ms here against 6.4).
+__global__ __launch_bounds__(kThreads) void k_quant_codes_sr(M1Params p, int8_t* __restrict__ codes) {
   const BlockEnt be = block_of(p.blk, p.flat, p.d);
   const int tid = threadIdx.x;
   const double qm = static_cast<double>(p.qmax);
@@ -270,17 +307,10 @@ __global__ __launch_bounds__(kThreads) void k_quant_codes(M1Params p, int8_t* __
               static_cast<uint64_t>(p.d) + static_cast<uint64_t>(be.start + loc)) + 1u) * kGamma;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        int qc;
-        if constexpr (MX) {
-          qc = sr_code(x.v[k], s, qm, mix64(z0 + static_cast<uint64_t>(k) * kGamma));
-        } else {
-          double y = __builtin_rint(static_cast<double>(x.v[k]) * s);
-          y = fmin(fmax(y, -qm), qm);
-          qc = static_cast<int>(y);
-        }
+        const int qc = sr_code(x.v[k], s, qm, mix64(z0 + static_cast<uint64_t>(k) * kGamma));
         packed |= (static_cast<uint32_t>(qc) & 0xFFu) << (8 * k);
       }
-      st_b4(codes + idx, packed, nv);
+      stnt_b4(codes + idx, packed, nv);
     }
   }
 }
@@ -323,8 +353,13 @@ hipError_t launch_m1_finalize(const M1Params& p, int maxnorm, hipStream_t st) {
 }
 
 hipError_t launch_quant_codes(const M1Params& p, int8_t* codes, int maxnorm, hipStream_t st) {
-  if (maxnorm) hipLaunchKernelGGL(k_quant_codes<true>, dim3(p.nblk), dim3(kThreads), 0, st, p, codes);
-  else hipLaunchKernelGGL(k_quant_codes<false>, dim3(p.nblk), dim3(kThreads), 0, st, p, codes);
+  if (maxnorm) {
+    hipLaunchKernelGGL(k_quant_codes_sr, dim3(static_cast<unsigned>(p.nblk)), dim3(kThreads), 0,
+                       st, p, codes);
+  } else {
+    const dim3 g(static_cast<unsigned>(p.nblk), static_cast<unsigned>(p.W));
+    hipLaunchKernelGGL(k_quant_codes, g, dim3(kThreads), 0, st, p, codes);
+  }
   return hipGetLastError();
 }
 

@@ -288,10 +288,10 @@ __device__ __forceinline__ void step_block(const StepParams& p, const BlockEnt& 
             // the row's last lane stores the word if its first element exists
             // (in a ragged tail that lane itself may hold none)
             if ((tid & 15) == 15 && (FULL || (j[q] & ~int64_t{63}) < be.start + be.len))
-              p.bits[static_cast<int64_t>(i) * (p.ld >> 6) + (j[q] >> 6)] = word;
+              stnt_u64(p.bits + static_cast<int64_t>(i) * (p.ld >> 6) + (j[q] >> 6), word);
           }
         } else if (kQ && DBG && p.codes && (FULL || nv[q] > 0)) {
-          st_b4(p.codes + idx, nib, nv[q]);
+          stnt_b4(p.codes + idx, nib, nv[q]);
         }
         if (FULL || nv[q] > 0) {
           if (!AVG) {
@@ -322,7 +322,7 @@ __device__ __forceinline__ void step_block(const StepParams& p, const BlockEnt& 
         s[k] = twice > W ? 1 : (twice < W ? -1 : (p.tie_zero ? 0 : (par ? 1 : -1)));
         sf[k] = static_cast<float>(s[k]);
       }
-      if (DBG && p.counts) st_b4(p.counts + j[q], cnt[q], nv[q]);
+      if (DBG && p.counts) stnt_b4(p.counts + j[q], cnt[q], nv[q]);
     } else if (AGG == kAggAvg) {
       // D-Lion averaging: the mean of the W signs, (2v - W) / W in fp32
 #pragma unroll
@@ -331,14 +331,14 @@ __device__ __forceinline__ void step_block(const StepParams& p, const BlockEnt& 
         s[k] = (net > 0) - (net < 0);
         sf[k] = static_cast<float>(net) / static_cast<float>(W);
       }
-      if (DBG && p.counts) st_b4(p.counts + j[q], cnt[q], nv[q]);
+      if (DBG && p.counts) stnt_b4(p.counts + j[q], cnt[q], nv[q]);
     } else if (kQ) {
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         s[k] = (sum[q][k] > 0) - (sum[q][k] < 0);
         sf[k] = static_cast<float>(s[k]);
       }
-      if (DBG && p.sums) st_i32x4(p.sums + j[q], sum[q], nv[q]);
+      if (DBG && p.sums) stnt_i32x4(p.sums + j[q], sum[q], nv[q]);
     } else {
       // apply mode: the sign arrives as bit planes (16 lanes share a word)
       const int sh = static_cast<int>(j[q] & 63);
@@ -375,7 +375,7 @@ __device__ __forceinline__ void step_block(const StepParams& p, const BlockEnt& 
                               ((static_cast<uint32_t>(s[1]) & 0xFFu) << 8) |
                               ((static_cast<uint32_t>(s[2]) & 0xFFu) << 16) |
                               ((static_cast<uint32_t>(s[3]) & 0xFFu) << 24);
-      st_b4(p.sign + j[q], packed, nv[q]);
+      stnt_b4(p.sign + j[q], packed, nv[q]);
     }
     // theta <- theta - lr*(sign + wd*theta)
 #pragma unroll
@@ -383,7 +383,7 @@ __device__ __forceinline__ void step_block(const StepParams& p, const BlockEnt& 
       const float x = th[q].v[k];
       th[q].v[k] = x - (p.lr * (sf[k] + (p.wd * x)));
     }
-    st_x4<TT>(p.theta, j[q], th[q], nv[q]);
+    stnt_x4<TT>(p.theta, j[q], th[q], nv[q]);
     // worker mean of the new momenta on averaging steps
     if (AVG) {
       const float fw = static_cast<float>(W);

@@ -60,8 +60,13 @@ __global__ __launch_bounds__(kThreads) void k_pack_codes(WireParams p) {
     if ((bit & 31) + N > 32) w[(bit >> 5) + 1] |= f >> (32 - (bit & 31));
   }
   uint32_t* dst = p.wire + i * (groups * N) + gi * N;
+  if constexpr (N == 4 || N == 8) {  // 16-byte aligned runs
 #pragma unroll
-  for (int k = 0; k < N; ++k) dst[k] = w[k];
+    for (int k = 0; k < N; k += 4) stnt_u128(dst + k, make_uint4(w[k], w[k + 1], w[k + 2], w[k + 3]));
+  } else {
+#pragma unroll
+    for (int k = 0; k < N; ++k) __builtin_nontemporal_store(w[k], dst + k);
+  }
 }
 
 // One thread per group of 32 elements: for every worker, N words -> 32
@@ -123,16 +128,18 @@ __global__ __launch_bounds__(kThreads) void k_unpack_sum(WireParams p) {
 #pragma unroll
       for (int k = 0; k < 8; ++k) {  // piece 64k + lane: lane src's quad lane % 8
         const int src = 8 * k + (lane >> 3);
-        *reinterpret_cast<int4*>(p.sums + wave_j0 + 4 * (64 * k + lane)) =
-            sh_s[wave * 512 + 8 * src + ((lane & 7) ^ (src & 7))];
+        const int4 v = sh_s[wave * 512 + 8 * src + ((lane & 7) ^ (src & 7))];
+        stnt_u128(p.sums + wave_j0 + 4 * (64 * k + lane),
+                  make_uint4(static_cast<uint32_t>(v.x), static_cast<uint32_t>(v.y),
+                             static_cast<uint32_t>(v.z), static_cast<uint32_t>(v.w)));
       }
     }
     if (p.sign) {
 #pragma unroll
       for (int k = 0; k < 2; ++k) {
         const int src = 32 * k + (lane >> 1);
-        *reinterpret_cast<uint4*>(p.sign + wave_j0 + 16 * (64 * k + lane)) =
-            sh_g[wave * 128 + 2 * src + ((lane & 1) ^ (src & 1))];
+        stnt_u128(p.sign + wave_j0 + 16 * (64 * k + lane),
+                  sh_g[wave * 128 + 2 * src + ((lane & 1) ^ (src & 1))]);
       }
     }
   } else if (valid >= 32) {
