@@ -189,3 +189,105 @@ def test_pack_and_vote_beyond_two_to_the_31_elements():
     lc.close()
     del x, bits, sign_p, zero_p
     torch.cuda.empty_cache()
+
+
+def test_entry_points_at_bench_size():
+    """Every standalone entry point on the 350M x 16 shape the benchmark
+    times with --op (same launch configuration): pack, vote (counts, signs
+    and bit planes), quant_l1 and quant_linf (the per-row norms of all 16
+    rows recomputed on the host and compared bit for bit; codes on sampled
+    columns), pack_codes and unpack_sum, and apply from the voted planes, each
+    checked against the oracle on the first columns, an interior range and
+    the last columns."""
+    import torch
+    torch.cuda.set_device(0)
+    wl = wls.FLAT_350M_W16_L1Q4
+    W, d, ld, n = wl.W, wl.d, wl.ld, wl.qbits
+    t = 3
+    lc = lioncub_for(wl)
+    x = gen.device_g(wl, 1)                        # heavy-tailed fp32 rows stand in for c
+    x[:, ::4099] = 0.0                             # exact zeros: the parity rule
+    words = ld // 64
+    bits = torch.empty((W, words), dtype=torch.int64, device="cuda")
+    counts = torch.empty(d, dtype=torch.uint8, device="cuda")
+    sign = torch.empty(d, dtype=torch.int8, device="cuda")
+    sign_p = torch.empty(words, dtype=torch.int64, device="cuda")
+    zero_p = torch.empty(words, dtype=torch.int64, device="cuda")
+    codes = torch.empty((W, ld), dtype=torch.int8, device="cuda")
+    codes_inf = torch.empty((W, ld), dtype=torch.int8, device="cuda")
+    m1 = torch.empty((W, 1), dtype=torch.float64, device="cuda")
+    minf = torch.empty((W, 1), dtype=torch.float64, device="cuda")
+    wire = torch.empty((W, (ld // 32) * n), dtype=torch.int32, device="cuda")
+    sums = torch.empty(d, dtype=torch.int32, device="cuda")
+    usign = torch.empty(d, dtype=torch.int8, device="cuda")
+    lc.pack(x, t, bits)
+    lc.vote(bits, t, counts, sign)
+    lc.vote_bits(bits, t, sign_p, zero_p)
+    lc.quant_l1(x, codes, m1)
+    lc.quant_linf(x, t, codes_inf, minf)
+    lc.pack_codes(codes, wire)
+    lc.unpack_sum(wire, sums, usign)
+    torch.cuda.synchronize()
+    _say("entry points ran on", wl.name)
+
+    # the per-row norms of every row, from the whole row on the host
+    got_m1, got_minf = to_host(m1)[:, 0], to_host(minf)[:, 0]
+    for i in range(W):
+        row = to_host(x[i, :d])
+        assert np.float64(got_m1[i]).view(np.uint64) == np.float64(lco.m1(row)).view(np.uint64), i
+        assert got_minf[i] == lco.minf(row), i
+    _say("norms of", W, "rows ok")
+
+    width = 65536
+    ranges = [(0, width), ((d // 2) // 64 * 64, (d // 2) // 64 * 64 + width), (d - width, d)]
+    for j0, j1 in ranges:
+        w0, w1 = j0 // 64, j1 // 64
+        xs = np.ascontiguousarray(to_host(x[:, j0:j1]))
+        want_bits = lco.pack(xs, j1 - j0, t)
+        assert np.array_equal(to_host(bits[:, w0:w1]).view(np.uint64), want_bits), (j0, "pack")
+        wc, ws = lco.vote(want_bits, W, j1 - j0, t)
+        assert np.array_equal(to_host(counts[j0:j1]), wc), (j0, "counts")
+        assert np.array_equal(to_host(sign[j0:j1]), ws), (j0, "sign")
+        sb, zb = lco.vote_bits(want_bits, W, j1 - j0, t)
+        assert np.array_equal(to_host(sign_p[w0:w1]).view(np.uint64), sb), (j0, "sign planes")
+        assert np.array_equal(to_host(zero_p[w0:w1]).view(np.uint64), zb), (j0, "zero planes")
+        # codes, element by element on the first 2048 columns of the range
+        cs = to_host(codes[:, j0:j1])
+        ci = to_host(codes_inf[:, j0:j1])
+        for i in range(W):
+            for k in range(2048):
+                j = j0 + k
+                assert cs[i, k] == lco.q1(xs[i, k], got_m1[i], n), (i, j, "q1")
+                ctr = (t * W + i) * d + j
+                draw = lco.splitmix64(wl.sr_seed, ctr)
+                assert ci[i, k] == lco.qinf(xs[i, k], got_minf[i], n, draw), (i, j, "qinf")
+        # wire format and the receive-side sum over the whole range
+        want_wire = lco.pack_codes(cs, j1 - j0, n)
+        g0, g1 = j0 // 32, j1 // 32
+        got_wire = to_host(wire[:, g0 * n:g1 * n]).view(np.uint32)
+        assert np.array_equal(got_wire, want_wire), (j0, "wire")
+        us, ug = lco.unpack_sum(want_wire, W, j1 - j0, j1 - j0, n)
+        assert np.array_equal(to_host(sums[j0:j1]), us), (j0, "sums")
+        assert np.array_equal(to_host(usign[j0:j1]), ug), (j0, "unpack sign")
+        _say("range", j0, j1, "ok")
+    del bits, counts, sign, codes, codes_inf, wire, sums, usign
+    torch.cuda.empty_cache()
+
+    # apply from the voted planes: x is this step's g
+    theta = gen.device_theta(wl)
+    m = gen.device_m(wl)
+    pre = [(j0, j1, to_host(theta[j0:j1]).copy(), np.ascontiguousarray(to_host(m[:, j0:j1])))
+           for j0, j1 in ranges]
+    lc.apply(theta, m, x, t, sign_p, zero_p)
+    torch.cuda.synchronize()
+    for j0, j1, th, mc in pre:
+        sl = wl.with_(name="slice", tensors=[("flat", j1 - j0)])
+        gs = np.ascontiguousarray(to_host(x[:, j0:j1]))
+        lco.apply(sl, th, mc, gs, t, to_host(sign_p[j0 // 64:j1 // 64]).view(np.uint64),
+                  to_host(zero_p[j0 // 64:j1 // 64]).view(np.uint64))
+        check_float_state(f"theta[{j0}:{j1}] apply", to_host(theta[j0:j1]), th)
+        check_float_state(f"m[:, {j0}:{j1}] apply", to_host(m[:, j0:j1]), mc)
+    _say("apply ok")
+    lc.close()
+    del x, theta, m, sign_p, zero_p, m1, minf
+    torch.cuda.empty_cache()
