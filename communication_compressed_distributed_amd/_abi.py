@@ -12,7 +12,7 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "liblioncub.so")
 
-OK, EINVAL, EALIGN, EWORKSPACE, EDEVICE, EUNSUPPORTED = 0, -1, -2, -3, -4, -5
+OK, EINVAL, EALIGN, EWORKSPACE, EDEVICE, EUNSUPPORTED, ENOMEM = 0, -1, -2, -3, -4, -5, -6
 F32, BF16 = 0, 1
 AGG_VOTE, AGG_L1SUM, AGG_AVG, AGG_LINFSUM = 0, 1, 2, 3
 TIE_PARITY, TIE_ZERO = 0, 1

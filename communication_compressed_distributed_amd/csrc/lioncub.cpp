@@ -229,7 +229,7 @@ int lioncub_init(lioncub_ctx** out, const lioncub_config* cfg, void* hip_stream,
   if (!workspace || !aligned(workspace, kWsAlign) || ws_bytes < L.total) return LIONCUB_EWORKSPACE;
 
   lioncub_ctx* c = new (std::nothrow) lioncub_ctx();
-  if (!c) return LIONCUB_EINVAL;
+  if (!c) return LIONCUB_ENOMEM;
   c->cfg = *cfg;
   c->stream = static_cast<hipStream_t>(hip_stream);
   c->nblk = static_cast<int32_t>(nblk);
@@ -245,9 +245,15 @@ int lioncub_init(lioncub_ctx** out, const lioncub_config* cfg, void* hip_stream,
   c->bstat = reinterpret_cast<uint64_t*>(ws + L.bstat);
   c->gstat = reinterpret_cast<uint64_t*>(ws + L.gstat);
 
-  c->h_tens.resize(cfg->n_tensors);
-  c->h_blk.reserve(nblk);
-  c->h_grp.reserve(ngrp);
+  // the host tables are sized once, so nothing below can throw
+  try {
+    c->h_tens.resize(cfg->n_tensors);
+    c->h_blk.reserve(nblk);
+    c->h_grp.reserve(ngrp);
+  } catch (const std::bad_alloc&) {
+    delete c;
+    return LIONCUB_ENOMEM;
+  }
   for (int T = 0; T < cfg->n_tensors; ++T) {
     const int64_t a = cfg->tensor_offsets[T], n = cfg->tensor_offsets[T + 1] - a;
     TensorEnt& te = c->h_tens[T];
@@ -479,8 +485,14 @@ int lioncub_stream_probe(int32_t kind, const float* a, const float* b, float* c,
 
 int lioncub_profile_begin(lioncub_ctx* ctx, int32_t capacity) {
   if (!ctx || capacity < 1 || ctx->prof) return LIONCUB_EINVAL;
-  ctx->prof_ev.assign(2 * static_cast<size_t>(capacity), nullptr);
-  ctx->prof_kind.assign(capacity, 0);
+  try {
+    ctx->prof_ev.assign(2 * static_cast<size_t>(capacity), nullptr);
+    ctx->prof_kind.assign(capacity, 0);
+  } catch (const std::bad_alloc&) {
+    ctx->prof_ev.clear();
+    ctx->prof_kind.clear();
+    return LIONCUB_ENOMEM;
+  }
   for (auto& ev : ctx->prof_ev) {
     if (hipEventCreate(&ev) != hipSuccess) {
       for (auto& e2 : ctx->prof_ev)
@@ -536,6 +548,7 @@ const char* lioncub_strerror(int status) {
     case LIONCUB_EWORKSPACE: return "workspace missing, misaligned or too small";
     case LIONCUB_EDEVICE: return "HIP runtime or kernel launch failure";
     case LIONCUB_EUNSUPPORTED: return "configuration not supported by this build";
+    case LIONCUB_ENOMEM: return "out of host memory";
     default: return "unknown status";
   }
 }

@@ -62,7 +62,9 @@ enum {
   LIONCUB_EALIGN = -2,       /* pointer not aligned as required           */
   LIONCUB_EWORKSPACE = -3,   /* workspace missing, misaligned or too small */
   LIONCUB_EDEVICE = -4,      /* HIP runtime / launch failure              */
-  LIONCUB_EUNSUPPORTED = -5  /* valid request this build does not support */
+  LIONCUB_EUNSUPPORTED = -5, /* valid request this build does not support */
+  LIONCUB_ENOMEM = -6        /* host memory for the context's tables or
+                                profiling events could not be allocated   */
 };
 
 enum { LIONCUB_F32 = 0, LIONCUB_BF16 = 1 };
@@ -133,7 +135,8 @@ size_t lioncub_workspace_bytes(const lioncub_config *cfg);
  * 256-byte aligned, owned by the caller, must outlive the context and not be
  * touched by the caller while the context lives) and upload the tensor and
  * block tables into it on hip_stream (a hipStream_t; NULL = the null stream).
- * Synchronises that stream once.  On success *out receives a new context. */
+ * Synchronises that stream once.  On success *out receives a new context;
+ * LIONCUB_ENOMEM if its host-side tables cannot be allocated. */
 int lioncub_init(lioncub_ctx **out, const lioncub_config *cfg, void *hip_stream,
                  void *workspace, size_t ws_bytes);
 
