@@ -88,6 +88,8 @@ class LionCub:
         period = 2 * self.sync_every // math.gcd(2, self.sync_every)
         if self.agg == "linf":
             raise ValueError("capture: the max-norm baseline's draws depend on the full step index")
+        if getattr(self, "_profiling", False):
+            raise ValueError("capture: profiling is on (its events would be recorded into the graph)")
         if K == 0 or K % period:
             raise ValueError(f"capture: the number of steps must be a multiple of {period}")
         for g in gs:
@@ -137,9 +139,12 @@ class LionCub:
 
     def profile_begin(self, capacity):
         lioncub_profile_begin(self.ctx, capacity)
+        self._profiling = True
 
     def profile_end(self):
-        return lioncub_profile_end(self.ctx)
+        out = lioncub_profile_end(self.ctx)
+        self._profiling = False
+        return out
 
     def close(self):
         if getattr(self, "ctx", None) is not None:

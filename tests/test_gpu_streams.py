@@ -218,6 +218,10 @@ def test_capture_refuses_windows_that_would_not_replay_exactly():
     gs = [torch.zeros((2, wl.ld), device="cuda") for _ in range(4)]
     with pytest.raises(ValueError):
         lc.capture(th, m, gs, 1)                    # 4 is not a multiple of lcm(2, 3) = 6
+    lc.profile_begin(8)
+    with pytest.raises(ValueError):
+        lc.capture(th, m, gs[:2] * 3, 1)            # profiling events would enter the graph
+    lc.profile_end()
     lc.close()
     wi = wls.flat("ci", 4096, W=2, agg="linf", qbits=4)
     li = lioncub_for(wi)
