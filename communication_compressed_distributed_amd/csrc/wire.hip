@@ -71,6 +71,9 @@ __global__ __launch_bounds__(kThreads) void k_pack_codes(WireParams p) {
 
 // One thread per group of 32 elements: for every worker, N words -> 32
 // sign-extended fields added to 32 int32 sums; then sums and signs stored.
+// The words of four workers are loaded before any is unpacked (same-process
+// timing on 350M x 16, n = 4: 0.80-0.81 ms against 0.83 ms one worker at a
+// time; 0.0055 against 0.0080 ms on 1M elements, where latency dominates).
 template <int N>
 __global__ __launch_bounds__(kThreads) void k_unpack_sum(WireParams p) {
   const int64_t groups = p.ld >> 5;
@@ -80,12 +83,7 @@ __global__ __launch_bounds__(kThreads) void k_unpack_sum(WireParams p) {
   int32_t S[32];
 #pragma unroll
   for (int k = 0; k < 32; ++k) S[k] = 0;
-#pragma unroll 1
-  for (int i = 0; i < p.W; ++i) {
-    const uint32_t* src = p.wire + static_cast<int64_t>(i) * (groups * N) + gi * N;
-    uint32_t w[N];
-#pragma unroll
-    for (int k = 0; k < N; ++k) w[k] = src[k];
+  auto add = [&](const uint32_t (&w)[N]) {
 #pragma unroll
     for (int k = 0; k < 32; ++k) {
       const int bit = N * k;
@@ -95,6 +93,26 @@ __global__ __launch_bounds__(kThreads) void k_unpack_sum(WireParams p) {
       const int32_t q = static_cast<int32_t>(f << (32 - N)) >> (32 - N);
       S[k] += q;
     }
+  };
+  const int64_t rstride = groups * N;
+  const uint32_t* base = p.wire + gi * N;
+  int i = 0;
+#pragma unroll 1
+  for (; i + 4 <= p.W; i += 4) {
+    uint32_t w[4][N];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int k = 0; k < N; ++k) w[u][k] = __builtin_nontemporal_load(base + (i + u) * rstride + k);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) add(w[u]);
+  }
+#pragma unroll 1
+  for (; i < p.W; ++i) {
+    uint32_t w[N];
+#pragma unroll
+    for (int k = 0; k < N; ++k) w[k] = base[i * rstride + k];
+    add(w);
   }
   const int64_t valid = p.d - j0;
   // A workgroup whose 256 groups all lie below d writes through LDS: each
