@@ -92,9 +92,11 @@ __device__ __forceinline__ void vadd(uint64_t (&c)[NPL], uint64_t x) {
 
 // One lane per 64-element word: loads the W workers' words of its column
 // (consecutive lanes read consecutive words: one coalesced 512-byte access
-// per wave and worker), counts the +1 bits of each element with bit-sliced
-// adders, then writes the 64 counts and signs (4 + 4 sixteen-byte stores),
-// and/or the sign planes from a bit-sliced comparison against W/2.
+// per wave and worker; 16 workers' words in flight, nontemporal), counts
+// the +1 bits of each element with bit-sliced adders, then writes the 64
+// counts and signs (4 + 4 sixteen-byte stores), and/or the sign planes from
+// a bit-sliced comparison against W/2.  (Same-process timing on 350M x 16:
+// the planes in 0.131 ms against 0.140 with 8 plain loads in flight.)
 template <int NPL>
 __global__ __launch_bounds__(kThreads) void k_vote_sliced(VoteParams p) {
   const int64_t wi = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
@@ -104,10 +106,18 @@ __global__ __launch_bounds__(kThreads) void k_vote_sliced(VoteParams p) {
 #pragma unroll
   for (int k = 0; k < NPL; ++k) c[k] = 0;
   int i = 0;
+#pragma unroll 1
+  for (; i + 16 <= p.W; i += 16) {
+    uint64_t x[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) x[u] = __builtin_nontemporal_load(p.bits + static_cast<int64_t>(i + u) * p.words + wi);
+#pragma unroll
+    for (int u = 0; u < 16; ++u) vadd<NPL>(c, x[u]);
+  }
   for (; i + 8 <= p.W; i += 8) {
     uint64_t x[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) x[u] = p.bits[static_cast<int64_t>(i + u) * p.words + wi];
+    for (int u = 0; u < 8; ++u) x[u] = __builtin_nontemporal_load(p.bits + static_cast<int64_t>(i + u) * p.words + wi);
 #pragma unroll
     for (int u = 0; u < 8; ++u) vadd<NPL>(c, x[u]);
   }
