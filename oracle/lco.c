@@ -543,6 +543,30 @@ void lco_unpack_sum(int32_t W, int64_t d, int64_t ld, int32_t qbits,
   }
 }
 
+/* The p-bit receive side with the global sign as a 2-bit value per element
+ * (the planes lco_apply takes): the integer sum of the W unpacked fields as
+ * in lco_unpack_sum, sign bit where it is > 0, zero bit where it is 0 (the
+ * p-bit sum can carry zero, so the parameter then only decays).  Every word
+ * of the [ld/64] planes is written; bits past d are 0. */
+void lco_unpack_sum_bits(int32_t W, int64_t d, int64_t ld, int32_t qbits,
+                         const uint32_t *wire, uint64_t *sign_bits, uint64_t *zero_bits) {
+  int64_t words = ld / 64;
+  int32_t *S = (int32_t *)malloc((size_t)(d > 0 ? d : 1) * sizeof(int32_t));
+  lco_unpack_sum(W, d, ld, qbits, wire, S, 0);
+  for (int64_t w = 0; w < words; w++) {
+    uint64_t sb = 0, zb = 0;
+    for (int64_t k = 0; k < 64; k++) {
+      int64_t j = 64 * w + k;
+      if (j >= d) break;
+      if (S[j] > 0) sb |= 1ull << k;
+      if (S[j] == 0) zb |= 1ull << k;
+    }
+    sign_bits[w] = sb;
+    if (zero_bits) zero_bits[w] = zb;
+  }
+  free(S);
+}
+
 void lco_step(const lco_cfg *cfg, int64_t ld, void *theta, float *m,
               const void *g, int64_t t, const lco_debug *dbg) {
   double *m1 = 0;

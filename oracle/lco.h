@@ -205,6 +205,12 @@ void lco_pack_codes(int32_t W, int64_t d, int64_t ld, int32_t qbits,
 void lco_unpack_sum(int32_t W, int64_t d, int64_t ld, int32_t qbits,
                     const uint32_t *wire, int32_t *sums, int8_t *sign);
 
+/* The same sums as lco_unpack_sum, delivered as the bit planes lco_apply
+ * takes: sign_bits[ld/64] has bit 1 where the sum is > 0, zero_bits[ld/64]
+ * (may be NULL) where it is 0; bits past d are 0. */
+void lco_unpack_sum_bits(int32_t W, int64_t d, int64_t ld, int32_t qbits,
+                         const uint32_t *wire, uint64_t *sign_bits, uint64_t *zero_bits);
+
 /* One whole step in place on the full state (theta[d], m[W][ld], g[W][ld]). */
 void lco_step(const lco_cfg *cfg, int64_t ld, void *theta, float *m,
               const void *g, int64_t t, const lco_debug *dbg);

@@ -71,6 +71,7 @@ def lib():
         L.lco_apply.argtypes = [C.POINTER(Cfg), i64, vp, vp, vp, i64, vp, vp]
         L.lco_pack_codes.argtypes = [i32, i64, i64, i32, vp, vp]
         L.lco_unpack_sum.argtypes = [i32, i64, i64, i32, vp, vp, vp]
+        L.lco_unpack_sum_bits.argtypes = [i32, i64, i64, i32, vp, vp, vp]
         L.lco_splitmix64.argtypes = [C.c_uint64, C.c_uint64]
         L.lco_splitmix64.restype = C.c_uint64
         L.lco_minf.argtypes = [vp, i64]
@@ -305,6 +306,15 @@ def pack_codes(codes, d, qbits):
     wire = np.empty((W, (ld // 32) * qbits), dtype=np.uint32)
     lib().lco_pack_codes(W, d, ld, qbits, _p(codes), _p(wire))
     return wire
+
+
+def unpack_sum_bits(wire, W, d, ld, qbits, zero=True):
+    """-> (sign_bits[ld/64], zero_bits[ld/64] or None) uint64 from the p-bit sums."""
+    wire = np.ascontiguousarray(wire, dtype=np.uint32)
+    sb = np.empty(ld // 64, dtype=np.uint64)
+    zb = np.empty(ld // 64, dtype=np.uint64) if zero else None
+    lib().lco_unpack_sum_bits(W, d, ld, qbits, _p(wire), _p(sb), _p(zb))
+    return sb, zb
 
 
 def unpack_sum(wire, W, d, ld, qbits):

@@ -591,6 +591,56 @@ def test_pack_codes_roundtrip_and_sum(oracle, n):
     assert np.array_equal(sign, np.sign(sums).astype(np.int8))
 
 
+@pytest.mark.parametrize("n", [2, 4, 8])
+def test_unpack_sum_bits_are_the_signs_of_numpy_column_sums(oracle, n):
+    """The p-bit receive side as planes: sign bit where NumPy's column sum of
+    the codes is > 0, zero bit where it is 0, nothing past d (ld > d + 64
+    leaves whole words past d, which must be written as 0)."""
+    qmax = 2 ** (n - 1) - 1
+    rs = np.random.default_rng(40 + n)
+    W, d, ld = 6, 1000, 1152
+    codes = np.zeros((W, ld), np.int8)
+    codes[:, :d] = rs.integers(-qmax, qmax + 1, (W, d))
+    codes[:, 100:164] = 0                              # a word of exact zero sums
+    wire = oracle.pack_codes(codes, d, n)
+    sb, zb = oracle.unpack_sum_bits(wire, W, d, ld, n)
+    col = codes[:, :d].astype(np.int64).sum(axis=0)
+    want_s = np.zeros(ld, np.uint8)
+    want_z = np.zeros(ld, np.uint8)
+    want_s[:d] = col > 0
+    want_z[:d] = col == 0
+    assert np.array_equal(_words_to_bits(sb, ld), want_s)
+    assert np.array_equal(_words_to_bits(zb, ld), want_z)
+    sb2, none = oracle.unpack_sum_bits(wire, W, d, ld, n, zero=False)
+    assert none is None and np.array_equal(sb2, sb)
+
+
+@pytest.mark.parametrize("agg", ["l1"])
+def test_p_bit_exchange_composes_into_the_step(oracle, agg):
+    """The worker-sharded p-bit flow written out of the oracle's own pieces
+    -- quantise each worker's c (quant_l1), pack the codes, unpack and sum
+    them into sign and zero planes, apply -- gives theta and m bit for bit
+    equal to the fused L1 step, on two tensors with a ragged end."""
+    from synth import gen
+    wl = wls.Workload(name="pbx", tensors=[("a", 4096 + 640), ("b", 2048)], W=4, agg=agg,
+                      qbits=3)
+    theta, m = gen.host_theta(wl), gen.host_m(wl)
+    g = gen.host_g(wl, 1)
+    t = 2
+    th1, m_1 = theta.copy(), m.copy()
+    oracle.step(wl, th1, m_1, g, t)
+    c = np.zeros((wl.W, wl.ld), np.float32)
+    for i in range(wl.W):
+        c[i, : wl.d] = oracle.c_row(wl, m[i, : wl.d], g[i, : wl.d])
+    codes, _ = oracle.quant_l1(wl, c)
+    wire = oracle.pack_codes(codes, wl.d, wl.qbits)
+    sb, zb = oracle.unpack_sum_bits(wire, wl.W, wl.d, wl.ld, wl.qbits)
+    th2, m_2 = theta.copy(), m.copy()
+    oracle.apply(wl, th2, m_2, g, t, sb, zb)
+    assert np.array_equal(th1, th2)
+    assert np.array_equal(m_1, m_2)
+
+
 def test_avg_aggregation_values(oracle):
     """D-Lion averaging: the applied update is the mean of the W signs,
     (2v - W)/W correctly rounded to fp32 (Python's Fraction -> float rounds
