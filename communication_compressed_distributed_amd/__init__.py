@@ -12,13 +12,15 @@ from ._abi import (AGG_AVG, AGG_L1SUM, AGG_LINFSUM, AGG_VOTE, BF16, F32, TIE_PAR
                    LionCubError, lioncub_apply, lioncub_destroy, lioncub_init, lioncub_pack,
                    lioncub_pack_codes, lioncub_profile_begin, lioncub_profile_end,
                    lioncub_quant_l1, lioncub_quant_linf, lioncub_set_stream, lioncub_step, lioncub_strerror,
-                   lioncub_unpack_sum, lioncub_vote, lioncub_vote_bits, lioncub_workspace_bytes,
+                   lioncub_unpack_sum, lioncub_unpack_sum_bits, lioncub_vote, lioncub_vote_bits,
+                   lioncub_workspace_bytes,
                    make_config)
 
 __all__ = ["LionCub", "LionCubError", "make_config", "lioncub_workspace_bytes", "lioncub_init",
            "lioncub_set_stream", "lioncub_step", "lioncub_pack", "lioncub_vote",
            "lioncub_quant_l1", "lioncub_quant_linf", "lioncub_vote_bits", "lioncub_apply",
-           "lioncub_pack_codes", "lioncub_unpack_sum", "lioncub_profile_begin", "lioncub_profile_end",
+           "lioncub_pack_codes", "lioncub_unpack_sum", "lioncub_unpack_sum_bits",
+           "lioncub_profile_begin", "lioncub_profile_end",
            "lioncub_destroy", "lioncub_strerror", "F32", "BF16", "AGG_VOTE", "AGG_L1SUM",
            "AGG_AVG", "AGG_LINFSUM", "TIE_PARITY", "TIE_ZERO"]
 
@@ -136,6 +138,10 @@ class LionCub:
     def unpack_sum(self, wire, sums=None, sign=None):
         _checks.unpack_sum(self.spec, self.device, wire, sums, sign)
         lioncub_unpack_sum(self.ctx, wire, sums, sign)
+
+    def unpack_sum_bits(self, wire, sign_bits, zero_bits=None):
+        _checks.unpack_sum_bits(self.spec, self.device, wire, sign_bits, zero_bits)
+        lioncub_unpack_sum_bits(self.ctx, wire, sign_bits, zero_bits)
 
     def profile_begin(self, capacity):
         lioncub_profile_begin(self.ctx, capacity)

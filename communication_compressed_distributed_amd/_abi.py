@@ -19,15 +19,16 @@ TIE_PARITY, TIE_ZERO = 0, 1
 STREAM_READ, STREAM_COPY, STREAM_TRIAD = 0, 1, 2
 (K_VOTE_STEP, K_M1_PARTIAL, K_M1_FINALIZE, K_L1_STEP, K_PACK, K_VOTE, K_QUANT, K_VOTE_BITS,
  K_APPLY, K_PACK_CODES, K_UNPACK_SUM, K_AVG_STEP, K_STATS, K_LINF_STEP, K_QUANT_LINF,
- K_COUNT) = range(16)
+ K_UNPACK_BITS, K_COUNT) = range(17)
 KERNEL_NAMES = ["vote_step", "m1_partial", "m1_finalize", "l1_step", "pack", "vote", "quant",
                 "vote_bits", "apply", "pack_codes", "unpack_sum", "avg_step", "stats",
-                "linf_step", "quant_linf"]
+                "linf_step", "quant_linf", "unpack_bits"]
 
 EXPORTS = ["lioncub_workspace_bytes", "lioncub_init", "lioncub_set_stream", "lioncub_step",
            "lioncub_pack", "lioncub_vote", "lioncub_quant_l1", "lioncub_quant_linf",
            "lioncub_vote_bits",
-           "lioncub_apply", "lioncub_pack_codes", "lioncub_unpack_sum", "lioncub_profile_begin",
+           "lioncub_apply", "lioncub_pack_codes", "lioncub_unpack_sum", "lioncub_unpack_sum_bits",
+           "lioncub_profile_begin",
            "lioncub_profile_end", "lioncub_stream_probe", "lioncub_destroy", "lioncub_strerror"]
 
 
@@ -84,6 +85,8 @@ def lib():
         L.lioncub_pack_codes.restype = C.c_int
         L.lioncub_unpack_sum.argtypes = [vp, vp, vp, vp]
         L.lioncub_unpack_sum.restype = C.c_int
+        L.lioncub_unpack_sum_bits.argtypes = [vp, vp, vp, vp]
+        L.lioncub_unpack_sum_bits.restype = C.c_int
         L.lioncub_profile_begin.argtypes = [vp, i32]
         L.lioncub_profile_begin.restype = C.c_int
         L.lioncub_profile_end.argtypes = [vp, C.POINTER(C.c_double), C.POINTER(C.c_int32)]
@@ -201,6 +204,11 @@ def lioncub_pack_codes(ctx, codes, wire):
 
 def lioncub_unpack_sum(ctx, wire, sums=None, sign=None):
     _check("lioncub_unpack_sum", lib().lioncub_unpack_sum(ctx, _ptr(wire), _ptr(sums), _ptr(sign)))
+
+
+def lioncub_unpack_sum_bits(ctx, wire, sign_bits, zero_bits=None):
+    _check("lioncub_unpack_sum_bits",
+           lib().lioncub_unpack_sum_bits(ctx, _ptr(wire), _ptr(sign_bits), _ptr(zero_bits)))
 
 
 def lioncub_profile_begin(ctx, capacity):

@@ -107,3 +107,9 @@ def unpack_sum(s, dev, wire, sums, sign):
     need("wire", wire, dev, "u32", s.W * (s.ld // 32) * max(s.qbits, 0))
     need("sums", sums, dev, "i32", s.d, optional=True)
     need("sign", sign, dev, "i8", s.d, optional=True)
+
+
+def unpack_sum_bits(s, dev, wire, sign_bits, zero_bits):
+    need("wire", wire, dev, "u32", s.W * (s.ld // 32) * max(s.qbits, 0))
+    need("sign_bits", sign_bits, dev, "u64", s.ld // 64)
+    need("zero_bits", zero_bits, dev, "u64", s.ld // 64, optional=True)

@@ -33,6 +33,8 @@ hipError_t launch_pack_codes(const int8_t* codes, uint32_t* wire, int64_t d, int
                              int n, hipStream_t st);
 hipError_t launch_unpack_sum(const uint32_t* wire, int32_t* sums, int8_t* sign, int64_t d,
                              int64_t ld, int W, int n, hipStream_t st);
+hipError_t launch_unpack_bits(const uint32_t* wire, uint64_t* sign_bits, uint64_t* zero_bits,
+                              int64_t d, int64_t ld, int W, int n, hipStream_t st);
 hipError_t launch_stream(int kind, const float* a, const float* b, float* c, int64_t n,
                          hipStream_t st);
 }  // namespace lioncub
@@ -416,6 +418,19 @@ int lioncub_unpack_sum(lioncub_ctx* ctx, const uint32_t* wire, int32_t* sums, in
   const lioncub_config& cf = ctx->cfg;
   return dev_status(run(ctx, LIONCUB_K_UNPACK_SUM, [&] {
     return launch_unpack_sum(wire, sums, sign, cf.d, cf.ld, cf.W, cf.qbits, ctx->stream);
+  }));
+}
+
+int lioncub_unpack_sum_bits(lioncub_ctx* ctx, const uint32_t* wire, uint64_t* sign_bits,
+                            uint64_t* zero_bits) {
+  if (!ctx || !wire || !sign_bits) return LIONCUB_EINVAL;
+  if (ctx->cfg.qbits < 2 || ctx->cfg.qbits > 8) return LIONCUB_EINVAL;
+  if (!aligned(wire, 16) || !aligned(sign_bits, 16) || !aligned(zero_bits, 16))
+    return LIONCUB_EALIGN;
+  const lioncub_config& cf = ctx->cfg;
+  return dev_status(run(ctx, LIONCUB_K_UNPACK_BITS, [&] {
+    return launch_unpack_bits(wire, sign_bits, zero_bits, cf.d, cf.ld, cf.W, cf.qbits,
+                              ctx->stream);
   }));
 }
 

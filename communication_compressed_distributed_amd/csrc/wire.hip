@@ -69,18 +69,14 @@ __global__ __launch_bounds__(kThreads) void k_pack_codes(WireParams p) {
   }
 }
 
-// One thread per group of 32 elements: for every worker, N words -> 32
-// sign-extended fields added to 32 int32 sums; then sums and signs stored.
-// The words of four workers are loaded before any is unpacked (same-process
-// timing on 350M x 16, n = 4: 0.80-0.81 ms against 0.83 ms one worker at a
-// time; 0.0055 against 0.0080 ms on 1M elements, where latency dominates).
+// The W workers' n-bit fields of group gi (32 elements), sign-extended and
+// summed in int32.  The words of four workers are loaded before any is
+// unpacked (same-process timing on 350M x 16, n = 4: 0.80-0.81 ms against
+// 0.83 ms one worker at a time; 0.0055 against 0.0080 ms on 1M elements,
+// where latency dominates).
 template <int N>
-__global__ __launch_bounds__(kThreads) void k_unpack_sum(WireParams p) {
+__device__ __forceinline__ void unpack_group(const WireParams& p, int64_t gi, int32_t (&S)[32]) {
   const int64_t groups = p.ld >> 5;
-  const int64_t gi = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
-  const int64_t j0 = gi << 5;
-  if (j0 >= p.d) return;
-  int32_t S[32];
 #pragma unroll
   for (int k = 0; k < 32; ++k) S[k] = 0;
   auto add = [&](const uint32_t (&w)[N]) {
@@ -114,6 +110,17 @@ __global__ __launch_bounds__(kThreads) void k_unpack_sum(WireParams p) {
     for (int k = 0; k < N; ++k) w[k] = base[i * rstride + k];
     add(w);
   }
+}
+
+// One thread per group of 32 elements: the sums (unpack_group), then sums
+// and signs stored.
+template <int N>
+__global__ __launch_bounds__(kThreads) void k_unpack_sum(WireParams p) {
+  const int64_t gi = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  const int64_t j0 = gi << 5;
+  if (j0 >= p.d) return;
+  int32_t S[32];
+  unpack_group<N>(p, gi, S);
   const int64_t valid = p.d - j0;
   // A workgroup whose 256 groups all lie below d writes through LDS: each
   // wave's 8 KB of sums (and 2 KB of signs) is stored as instructions of 64
@@ -186,6 +193,34 @@ __global__ __launch_bounds__(kThreads) void k_unpack_sum(WireParams p) {
   }
 }
 
+// The same sums as 2-bit global signs, in the bit planes the apply mode of
+// the step kernel reads: one thread per group of 32 elements over all ld/32
+// groups writes the 32-bit half gi of the sign plane (bit k: sum > 0) and of
+// the zero plane (sum == 0); elements past d, and groups wholly past d
+// (whose wire words are not read), give 0 bits.
+template <int N>
+__global__ __launch_bounds__(kThreads) void k_unpack_bits(WireParams p, uint32_t* __restrict__ sign_h,
+                                                          uint32_t* __restrict__ zero_h) {
+  const int64_t gi = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  if (gi >= (p.ld >> 5)) return;
+  const int64_t j0 = gi << 5;
+  uint32_t sb = 0, zb = 0;
+  if (j0 < p.d) {
+    int32_t S[32];
+    unpack_group<N>(p, gi, S);
+    const int64_t valid = p.d - j0;
+#pragma unroll
+    for (int k = 0; k < 32; ++k) {
+      if (k < valid) {
+        sb |= static_cast<uint32_t>(S[k] > 0) << k;
+        zb |= static_cast<uint32_t>(S[k] == 0) << k;
+      }
+    }
+  }
+  __builtin_nontemporal_store(sb, sign_h + gi);
+  if (zero_h) __builtin_nontemporal_store(zb, zero_h + gi);
+}
+
 hipError_t launch_pack_codes(const int8_t* codes, uint32_t* wire, int64_t d, int64_t ld, int W,
                              int n, hipStream_t st) {
   WireParams p{codes, wire, nullptr, nullptr, d, ld, W};
@@ -217,6 +252,26 @@ hipError_t launch_unpack_sum(const uint32_t* wire, int32_t* sums, int8_t* sign, 
     case 6: hipLaunchKernelGGL(k_unpack_sum<6>, g, b, 0, st, p); break;
     case 7: hipLaunchKernelGGL(k_unpack_sum<7>, g, b, 0, st, p); break;
     case 8: hipLaunchKernelGGL(k_unpack_sum<8>, g, b, 0, st, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_unpack_bits(const uint32_t* wire, uint64_t* sign_bits, uint64_t* zero_bits,
+                              int64_t d, int64_t ld, int W, int n, hipStream_t st) {
+  WireParams p{nullptr, const_cast<uint32_t*>(wire), nullptr, nullptr, d, ld, W};
+  uint32_t* sh = reinterpret_cast<uint32_t*>(sign_bits);
+  uint32_t* zh = reinterpret_cast<uint32_t*>(zero_bits);
+  const int64_t threads = ld >> 5;
+  const dim3 g(static_cast<unsigned>((threads + kThreads - 1) / kThreads)), b(kThreads);
+  switch (n) {
+    case 2: hipLaunchKernelGGL(k_unpack_bits<2>, g, b, 0, st, p, sh, zh); break;
+    case 3: hipLaunchKernelGGL(k_unpack_bits<3>, g, b, 0, st, p, sh, zh); break;
+    case 4: hipLaunchKernelGGL(k_unpack_bits<4>, g, b, 0, st, p, sh, zh); break;
+    case 5: hipLaunchKernelGGL(k_unpack_bits<5>, g, b, 0, st, p, sh, zh); break;
+    case 6: hipLaunchKernelGGL(k_unpack_bits<6>, g, b, 0, st, p, sh, zh); break;
+    case 7: hipLaunchKernelGGL(k_unpack_bits<7>, g, b, 0, st, p, sh, zh); break;
+    case 8: hipLaunchKernelGGL(k_unpack_bits<8>, g, b, 0, st, p, sh, zh); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -237,6 +237,16 @@ int lioncub_pack_codes(lioncub_ctx *ctx, const int8_t *codes, uint32_t *wire);
  * 0 for a zero sum).  At least one output must be given. */
 int lioncub_unpack_sum(lioncub_ctx *ctx, const uint32_t *wire, int32_t *sums, int8_t *sign);
 
+/* The same receive side delivering the global sign as the 2-bit value per
+ * element that lioncub_apply takes (the p-bit sum can be 0, so a 1-bit
+ * plane does not carry it): from wire[W][(ld/32)*n] (device), sign_bits
+ * [ld/64] (device, required) gets bit 1 where the int32 sum is > 0 and
+ * zero_bits[ld/64] (device, may be NULL) bit 1 where it is 0.  Every word is
+ * written; bits past d are 0.  quant_l1 -> pack_codes -> unpack_sum_bits ->
+ * apply on the same state is exactly lioncub_step on the L1 path. */
+int lioncub_unpack_sum_bits(lioncub_ctx *ctx, const uint32_t *wire, uint64_t *sign_bits,
+                            uint64_t *zero_bits);
+
 /* Measurement hook: while enabled, every kernel the context launches is
  * bracketed by HIP events on its stream (at most `capacity` launches are
  * recorded).  lioncub_profile_end synchronises on the events, disables the
@@ -260,7 +270,8 @@ enum {
   LIONCUB_K_STATS = 12,
   LIONCUB_K_LINF_STEP = 13,
   LIONCUB_K_QUANT_LINF = 14,
-  LIONCUB_K_COUNT = 15
+  LIONCUB_K_UNPACK_BITS = 15,
+  LIONCUB_K_COUNT = 16
 };
 int lioncub_profile_begin(lioncub_ctx *ctx, int32_t capacity);
 int lioncub_profile_end(lioncub_ctx *ctx, double *ms_total, int32_t *launches);

@@ -104,6 +104,8 @@ def test_null_context_and_arguments_rejected():
     assert L.lioncub_pack(None, p, 1, p) == _abi.EINVAL
     assert L.lioncub_vote(None, p, 1, p, p) == _abi.EINVAL
     assert L.lioncub_quant_l1(None, p, p, None) == _abi.EINVAL
+    assert L.lioncub_unpack_sum(None, p, p, p) == _abi.EINVAL
+    assert L.lioncub_unpack_sum_bits(None, p, p, None) == _abi.EINVAL
     assert L.lioncub_set_stream(None, None) == _abi.EINVAL
     assert L.lioncub_profile_begin(None, 4) == _abi.EINVAL
     assert L.lioncub_destroy(None) == _abi.OK

@@ -413,6 +413,68 @@ def test_wire_pack_and_unpack_sum(n, W, d):
     lc.close()
 
 
+@pytest.mark.parametrize("d", [4096 + 1000 + 7, 3 * 8192 + 1000 + 7, 4 * 8192])
+@pytest.mark.parametrize("n", [2, 3, 4, 8])
+@pytest.mark.parametrize("W", [1, 3, 16])
+def test_unpack_sum_bits(n, W, d):
+    """Sign and zero planes of the p-bit sums against the oracle, with row
+    padding: words wholly past d are written as 0 (the planes start as
+    junk); the zero plane is optional."""
+    import torch
+    qmax = 2 ** (n - 1) - 1
+    rs = np.random.default_rng(100 + 10 * n + W)
+    ld = (d + 63) // 64 * 64 + 128
+    wl, lc = _ctx(W, d, ld=ld, agg="l1", qbits=n)
+    codes = rs.integers(-qmax, qmax + 1, (W, ld)).astype(np.int8)
+    codes[:, 64:192] = 0                                   # exact zero sums
+    wire = torch.empty((W, (ld // 32) * n), dtype=torch.int32, device="cuda")
+    lc.pack_codes(to_dev(codes), wire)
+    sb = torch.full((ld // 64,), -1, dtype=torch.int64, device="cuda")
+    zb = torch.full((ld // 64,), -1, dtype=torch.int64, device="cuda")
+    lc.unpack_sum_bits(wire, sb, zb)
+    sb_only = torch.full((ld // 64,), -1, dtype=torch.int64, device="cuda")
+    lc.unpack_sum_bits(wire, sb_only)
+    torch.cuda.synchronize()
+    ws, wz = lco.unpack_sum_bits(to_host(wire).view(np.uint32), W, d, ld, n)
+    assert np.array_equal(to_host(sb).view(np.uint64), ws)
+    assert np.array_equal(to_host(zb).view(np.uint64), wz)
+    assert np.array_equal(to_host(sb_only).view(np.uint64), ws)
+    lc.close()
+
+
+@pytest.mark.parametrize("n", [3, 4, 8])
+def test_p_bit_exchange_composes_into_the_step(n):
+    """The worker-sharded p-bit flow on one GPU: quant_l1(c) -> pack_codes ->
+    unpack_sum_bits -> apply gives theta and m bit for bit equal to the
+    fused L1 step, on two tensors with a ragged end and bf16 gradients."""
+    import torch
+    from synth import gen
+    wl = wls.Workload(name="pbx", tensors=[("a", 2 * 4096 + 192), ("b", 4096)], W=8, agg="l1",
+                      qbits=n, grad_dtype="bf16")
+    theta, m = gen.host_theta(wl), gen.host_m(wl)
+    g = gen.host_g(wl, 1)
+    c = np.zeros((wl.W, wl.ld), np.float32)
+    for i in range(wl.W):
+        c[i, : wl.d] = lco.c_row(wl, m[i, : wl.d], g[i, : wl.d])
+    lc = lioncub_for(wl)
+    dg = to_dev(g, bf16=True)
+    thA, mA = to_dev(theta), to_dev(m)
+    lc.step(thA, mA, dg, 3)
+    codes = torch.zeros((wl.W, wl.ld), dtype=torch.int8, device="cuda")
+    lc.quant_l1(to_dev(c), codes)
+    wire = torch.empty((wl.W, (wl.ld // 32) * n), dtype=torch.int32, device="cuda")
+    lc.pack_codes(codes, wire)
+    sb = torch.empty((wl.ld // 64,), dtype=torch.int64, device="cuda")
+    zb = torch.empty((wl.ld // 64,), dtype=torch.int64, device="cuda")
+    lc.unpack_sum_bits(wire, sb, zb)
+    thB, mB = to_dev(theta), to_dev(m)
+    lc.apply(thB, mB, dg, 3, sb, zb)
+    torch.cuda.synchronize()
+    assert int(to_host(zb).view(np.uint64).astype(bool).sum()) > 0   # zeros were exercised
+    assert torch.equal(thA, thB) and torch.equal(mA, mB)
+    lc.close()
+
+
 def test_p_bit_path_composes_into_the_step():
     """quant_l1(c) -> pack_codes -> unpack_sum reproduces the fused L1 step's
     integer sums and signs (debug outputs) bit for bit."""
