@@ -198,7 +198,7 @@ def test_entry_points_at_bench_size():
     rows recomputed on the host and compared bit for bit; codes on sampled
     columns), pack_codes and unpack_sum, and apply from the voted planes, each
     checked against the oracle on the first columns, an interior range and
-    the last columns."""
+    the last columns (unpack_sum_bits too)."""
     import torch
     torch.cuda.set_device(0)
     wl = wls.FLAT_350M_W16_L1Q4
@@ -220,6 +220,8 @@ def test_entry_points_at_bench_size():
     wire = torch.empty((W, (ld // 32) * n), dtype=torch.int32, device="cuda")
     sums = torch.empty(d, dtype=torch.int32, device="cuda")
     usign = torch.empty(d, dtype=torch.int8, device="cuda")
+    usb = torch.empty(words, dtype=torch.int64, device="cuda")
+    uzb = torch.empty(words, dtype=torch.int64, device="cuda")
     lc.pack(x, t, bits)
     lc.vote(bits, t, counts, sign)
     lc.vote_bits(bits, t, sign_p, zero_p)
@@ -227,6 +229,7 @@ def test_entry_points_at_bench_size():
     lc.quant_linf(x, t, codes_inf, minf)
     lc.pack_codes(codes, wire)
     lc.unpack_sum(wire, sums, usign)
+    lc.unpack_sum_bits(wire, usb, uzb)
     torch.cuda.synchronize()
     _say("entry points ran on", wl.name)
 
@@ -269,8 +272,11 @@ def test_entry_points_at_bench_size():
         us, ug = lco.unpack_sum(want_wire, W, j1 - j0, j1 - j0, n)
         assert np.array_equal(to_host(sums[j0:j1]), us), (j0, "sums")
         assert np.array_equal(to_host(usign[j0:j1]), ug), (j0, "unpack sign")
+        ub, uz = lco.unpack_sum_bits(want_wire, W, j1 - j0, j1 - j0, n)
+        assert np.array_equal(to_host(usb[w0:w1]).view(np.uint64), ub), (j0, "unpack sign plane")
+        assert np.array_equal(to_host(uzb[w0:w1]).view(np.uint64), uz), (j0, "unpack zero plane")
         _say("range", j0, j1, "ok")
-    del bits, counts, sign, codes, codes_inf, wire, sums, usign
+    del bits, counts, sign, codes, codes_inf, wire, sums, usign, usb, uzb
     torch.cuda.empty_cache()
 
     # apply from the voted planes: x is this step's g
