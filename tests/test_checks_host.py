@@ -31,11 +31,13 @@ def test_good_arguments_pass():
     _checks.apply(S, CPU, th, m, g, torch.zeros(16, dtype=torch.int64), torch.zeros(16, dtype=torch.int64))
     _checks.pack_codes(S, CPU, torch.zeros((3, 1024), dtype=torch.int8), torch.zeros((3, 128), dtype=torch.int32))
     _checks.unpack_sum(S, CPU, torch.zeros((3, 128), dtype=torch.int32), torch.zeros(1000, dtype=torch.int32), None)
+    _checks.unpack_sum_bits(S, CPU, torch.zeros((3, 128), dtype=torch.int32), torch.zeros(16, dtype=torch.int64), None)
 
 
 @pytest.mark.parametrize("case", [
     "theta short", "theta f32", "m short", "m strided", "m f64", "g bf16", "debug codes short",
-    "debug bits i32", "debug unknown", "stats short", "wire short", "sign u8", "bits missing"])
+    "debug bits i32", "debug unknown", "stats short", "wire short", "sign u8", "bits missing",
+    "planes short", "planes i32"])
 def test_bad_arguments_raise(case):
     th, m, g = good_state()
     with pytest.raises(ValueError):
@@ -67,6 +69,12 @@ def test_bad_arguments_raise(case):
                          torch.zeros(1000, dtype=torch.uint8))
         elif case == "bits missing":
             _checks.vote_bits(S, CPU, torch.zeros((3, 16), dtype=torch.int64), None, None)
+        elif case == "planes short":
+            _checks.unpack_sum_bits(S, CPU, torch.zeros((3, 128), dtype=torch.int32),
+                                    torch.zeros(15, dtype=torch.int64), None)
+        elif case == "planes i32":
+            _checks.unpack_sum_bits(S, CPU, torch.zeros((3, 128), dtype=torch.int32),
+                                    torch.zeros(16, dtype=torch.int64), torch.zeros(32, dtype=torch.int32))
 
 
 def test_device_must_match():
