@@ -8,6 +8,8 @@ compared bit for bit."""
 import numpy as np
 import pytest
 
+from oracle import lco
+from synth import gen
 from synth import workloads as wls
 from tests.harness import gpu_step_vs_oracle
 
@@ -54,3 +56,53 @@ def test_random_config(k):
           flush=True)
     gpu_step_vs_oracle(wl, steps=2, t0=t0, debug=True)
     gpu_step_vs_oracle(wl, steps=1, t0=t0 + 2, debug=False, seed_shift=1)
+
+
+N_EXCHANGE = 40
+
+
+@pytest.mark.parametrize("k", range(N_EXCHANGE))
+def test_random_config_exchange_composes_into_the_step(k):
+    """On the same random configurations, the worker-sharded exchange built
+    from the standalone calls -- vote path: pack(c) -> vote_bits; quantised
+    paths: quant_l1 / quant_linf(c) -> pack_codes -> unpack_sum_bits; then
+    apply -- leaves theta and m bit for bit where the fused step leaves
+    them.  The averaging path applies fractional signs and has no planes."""
+    import torch
+    from tests.harness import lioncub_for, to_dev
+    wl = random_workload(k)
+    if wl.agg == "avg":
+        pytest.skip("the averaging path has no sign planes")
+    t = int(np.random.default_rng(k).integers(1, 1000))
+    tb, gb = wl.theta_dtype == "bf16", wl.grad_dtype == "bf16"
+    theta, m = gen.host_theta(wl), gen.host_m(wl)
+    g = gen.host_g(wl, t)
+    c = np.zeros((wl.W, wl.ld), np.float32)
+    for i in range(wl.W):
+        c[i, : wl.d] = lco.c_row(wl, m[i, : wl.d], g[i, : wl.d])
+    lc = lioncub_for(wl)
+    dg = to_dev(g, gb)
+    thA, mA = to_dev(theta, tb), to_dev(m)
+    lc.step(thA, mA, dg, t)
+    words = wl.ld // 64
+    sb = torch.empty(words, dtype=torch.int64, device="cuda")
+    zb = torch.empty(words, dtype=torch.int64, device="cuda")
+    if wl.agg == "vote":
+        bits = torch.empty((wl.W, words), dtype=torch.int64, device="cuda")
+        lc.pack(to_dev(c), t, bits)
+        lc.vote_bits(bits, t, sb, zb)
+    else:
+        codes = torch.empty((wl.W, wl.ld), dtype=torch.int8, device="cuda")
+        if wl.agg == "l1":
+            lc.quant_l1(to_dev(c), codes)
+        else:
+            lc.quant_linf(to_dev(c), t, codes)
+        wire = torch.empty((wl.W, (wl.ld // 32) * wl.qbits), dtype=torch.int32, device="cuda")
+        lc.pack_codes(codes, wire)
+        lc.unpack_sum_bits(wire, sb, zb)
+    thB, mB = to_dev(theta, tb), to_dev(m)
+    lc.apply(thB, mB, dg, t, sb, zb)
+    torch.cuda.synchronize()
+    assert torch.equal(thA.view(torch.int16) if tb else thA, thB.view(torch.int16) if tb else thB)
+    assert torch.equal(mA[:, : wl.d], mB[:, : wl.d])
+    lc.close()
