@@ -127,8 +127,10 @@ typedef struct {
                       sums S1, S2 of m' and m'^2, floored at 0                */
 } lioncub_debug;
 
-/* Bytes of device workspace lioncub_init needs for cfg (0 if cfg is invalid).
- * Pure host computation. */
+/* Bytes of device workspace lioncub_init needs for cfg (0 if cfg is invalid):
+ * the block, tensor and group tables, the norm partials and scales, the
+ * diagnostics' counters and, on the vote and averaging paths with
+ * W*ld >= 3*2^28, W*ld/8 bytes of sign bitmaps.  Pure host computation. */
 size_t lioncub_workspace_bytes(const lioncub_config *cfg);
 
 /* Validate cfg, lay out the caller's workspace (device, >= the bytes above,
@@ -152,9 +154,14 @@ int lioncub_set_stream(lioncub_ctx *ctx, void *hip_stream);
  *          paths, codes/sums/m1 on the quantised paths, sign and the
  *          diagnostics on all); an output of another path is an error
  *          (LIONCUB_EINVAL)
- * The vote path is one kernel; the quantised paths are three (norm block
- * partials, per-(worker, tensor) norm and scale, then the fused
- * quantise-sum-apply). */
+ * On states of W*ld >= 3*2^28 elements the vote and averaging paths run as
+ * two kernels, the halves of the 1-bit exchange back to back: sign bits and
+ * momentum update per (block, worker) into the workspace's bitmaps, then
+ * the vote (or mean) and theta; on smaller states, with a debug output, or
+ * on a step that averages momenta, as one fused kernel (the same results,
+ * bit for bit).  The quantised paths are
+ * three kernels (norm block partials, per-(worker, tensor) norm and scale,
+ * then the fused quantise-sum-apply). */
 int lioncub_step(lioncub_ctx *ctx, void *theta, float *m, const void *g, int64_t t,
                  const lioncub_debug *dbg);
 

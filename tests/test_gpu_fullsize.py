@@ -297,3 +297,46 @@ def test_entry_points_at_bench_size():
     lc.close()
     del x, theta, m, sign_p, zero_p, m1, minf
     torch.cuda.empty_cache()
+
+
+SPLIT_CASES = {
+    # W * ld just above 3 * 2^28: the vote and averaging paths take the
+    # two-kernel step (sign bits + momentum per (block, worker), then vote and
+    # theta); W > 16 exercises the receive side's 16-worker chunks
+    "vote-W255": wls.flat("split-vote-W255", 3_158_037, W=255, agg="vote", g_nu=3.0),
+    "avg-W40-bf16": wls.flat("split-avg-W40", 20_132_673, W=40, agg="avg", theta_dtype="bf16",
+                             grad_dtype="bf16", g_nu=3.0),
+    "vote-W17-tiezero-3T": wls.Workload(name="split-vote-W17",
+                                        tensors=[("a", 20_000_064), ("b", 4160), ("c", 27_380_000)],
+                                        W=17, agg="vote", tie="zero", theta_dtype="bf16",
+                                        g_nu=3.0),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SPLIT_CASES))
+def test_two_kernel_one_bit_step(name):
+    """Above the size where the 1-bit paths run as two kernels: two
+    production steps against the oracle on sampled ranges, then one step
+    from the same state through the split kernels (production call) and
+    through the fused kernel (a debug output forces it): theta and m bit for
+    bit equal."""
+    import torch
+    wl = SPLIT_CASES[name]
+    assert wl.W * wl.ld >= 3 * 2 ** 28
+    run_fullsize(wl, steps=[1, 2], n_random=2)
+    torch.cuda.set_device(0)
+    lc = lioncub_for(wl)
+    theta = gen.device_theta(wl)
+    m = gen.device_m(wl)
+    g = gen.device_g(wl, 3)
+    thB, mB = theta.clone(), m.clone()
+    lc.step(theta, m, g, 3)                                          # two kernels
+    lc.step(thB, mB, g, 3, {"sign": torch.empty(wl.d, dtype=torch.int8, device="cuda")})
+    torch.cuda.synchronize()
+    assert torch.equal(theta.view(torch.int16) if wl.theta_dtype == "bf16" else theta,
+                       thB.view(torch.int16) if wl.theta_dtype == "bf16" else thB)
+    assert torch.equal(m, mB)
+    _say(name, "split == fused")
+    lc.close()
+    del theta, m, g, thB, mB
+    torch.cuda.empty_cache()
