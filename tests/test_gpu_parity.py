@@ -120,7 +120,7 @@ def test_pack_vote_handworked(t, tie):
 
 
 @pytest.mark.parametrize("d", [3 * 4096 + 1001, 3 * 16384 + 1001, 4 * 16384])
-@pytest.mark.parametrize("W", [1, 2, 3, 4, 5, 8, 17])
+@pytest.mark.parametrize("W", [1, 2, 3, 4, 5, 8, 17, 40, 255])
 @pytest.mark.parametrize("t", [1, 2])
 def test_pack_vote_random(W, t, d):
     """Ragged d, exact zeros, padded rows; bitwise against the oracle (whose
