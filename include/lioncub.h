@@ -226,7 +226,9 @@ int lioncub_vote_bits(lioncub_ctx *ctx, const uint64_t *bits, int64_t t,
  * writes them; zero_bits may be NULL = no zeros): theta <- theta - lr*(s +
  * wd*theta) with s = zero ? 0 : (sign ? +1 : -1), then every worker's
  * momentum update and the selective averaging, exactly as lioncub_step.
- * theta/m/g as in lioncub_step; sign_bits/zero_bits device [ld/64]. */
+ * theta/m/g as in lioncub_step; sign_bits/zero_bits device [ld/64].  From
+ * W*ld >= 2^28 up, on steps that do not average momenta, the momentum
+ * update and the theta update run as two kernels (the same results). */
 int lioncub_apply(lioncub_ctx *ctx, void *theta, float *m, const void *g, int64_t t,
                   const uint64_t *sign_bits, const uint64_t *zero_bits);
 

@@ -340,3 +340,53 @@ def test_two_kernel_one_bit_step(name):
     lc.close()
     del theta, m, g, thB, mB
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("dtypes", [("f32", "f32"), ("bf16", "bf16")])
+def test_two_kernel_apply(dtypes):
+    """lioncub_apply on a state above the size where it runs as two kernels
+    (momentum per (block, worker), then theta from the planes), two tensors
+    with a ragged end, random sign and zero planes: sampled ranges bit for
+    bit against the oracle; then an averaging step of a synced tensor (the
+    fused kernel) the same way."""
+    import torch
+    th_dt, g_dt = dtypes
+    wl = wls.Workload(name="split-apply", tensors=[("a", 16_777_216), ("b", 16_777_216 + 4160)],
+                      W=8, theta_dtype=th_dt, grad_dtype=g_dt, sync_names=("b",), sync_every=2,
+                      g_nu=3.0)
+    assert wl.W * wl.ld >= 2 ** 28
+    torch.cuda.set_device(0)
+    lc = lioncub_for(wl)
+    theta, m = gen.device_theta(wl), gen.device_m(wl)
+    words = wl.ld // 64
+    gen_t = torch.Generator(device="cuda").manual_seed(5)
+    sb = torch.randint(-2 ** 62, 2 ** 62, (words,), generator=gen_t, device="cuda", dtype=torch.int64)
+    zb = torch.randint(-2 ** 62, 2 ** 62, (words,), generator=gen_t, device="cuda", dtype=torch.int64)
+    zb &= torch.randint(-2 ** 62, 2 ** 62, (words,), generator=gen_t, device="cuda", dtype=torch.int64)
+    tail = wl.d // 64                                      # bits past d are 0
+    if wl.d % 64:
+        sb[tail] &= (1 << (wl.d % 64)) - 1
+        zb[tail] &= (1 << (wl.d % 64)) - 1
+    sb[tail + (1 if wl.d % 64 else 0):] = 0
+    zb[tail + (1 if wl.d % 64 else 0):] = 0
+    rs = np.random.default_rng(3)
+    ranges = sample_ranges(wl, [0, 1], rs, width=8192, n_random=2)
+    tb = th_dt == "bf16"
+    for t in (1, 2):                                       # t = 2 averages tensor b
+        g = gen.device_g(wl, t)
+        pre = [(j0, j1, to_host(theta[j0:j1]).copy(), np.ascontiguousarray(to_host(m[:, j0:j1])),
+                np.ascontiguousarray(to_host(g[:, j0:j1]))) for j0, j1 in ranges]
+        lc.apply(theta, m, g, t, sb, zb)
+        torch.cuda.synchronize()
+        for j0, j1, th, mc, gc in pre:
+            T = 0 if j1 <= wl.offsets[1] else 1
+            sl = wl.with_(name="slice", tensors=[("b" if T else "a", j1 - j0)])
+            lco.apply(sl, th, mc, gc, t, to_host(sb[j0 // 64:(j1 + 63) // 64]).view(np.uint64),
+                      to_host(zb[j0 // 64:(j1 + 63) // 64]).view(np.uint64))
+            check_float_state(f"theta[{j0}:{j1}] t={t}", to_host(theta[j0:j1]), th, bf16=tb)
+            check_float_state(f"m[:, {j0}:{j1}] t={t}", to_host(m[:, j0:j1]), mc)
+        _say("split apply", dtypes, "t", t, "ok")
+        del g
+    lc.close()
+    del theta, m, sb, zb
+    torch.cuda.empty_cache()
