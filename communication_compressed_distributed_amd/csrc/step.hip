@@ -27,6 +27,12 @@
 // stores follow.  HBM-bound: per element it moves W*(4 + s_g + 4) + 2*s_theta
 // bytes on every path -- nothing else (the quantised paths' norm pass is a
 // separate kernel).
+//
+// Two pairs of kernels at the end of the file split the work differently for
+// large states, because workgroups that stream a single worker row run
+// faster than ones that walk all W rows: the 1-bit step as "sign bits and
+// momentum per (block, worker)" then "vote and theta", and lioncub_apply as
+// "momentum per (block, worker)" then "theta from the planes".
 #include "device.hpp"
 #include "layout.hpp"
 
