@@ -65,3 +65,20 @@ def test_algorithmic_bytes_per_parameter(name, step_total, fused, norm):
                                          "flat-350M-w16-l1q4": 114.8,
                                          "gpt-760M-w8-vote-bf16-syncemb": 63.73,
                                          "gpt-1.3B-w8-l1q8-bf16g": 178.65}[name]) < 0.01
+
+
+def test_traffic_digest_ignores_comments_not_code():
+    """Editing a comment keeps the HBM-traffic record valid; editing code
+    invalidates it."""
+    import os
+    pkg = os.path.join(bench.ROOT, "communication_compressed_distributed_amd")
+
+    def read(rel, edit=None):
+        with open(os.path.join(pkg, rel)) as f:
+            text = f.read()
+        return edit(text) if edit and rel.endswith("step.hip") else text
+
+    base = bench.kernel_source_digest()
+    assert bench.kernel_source_digest(lambda r: read(r, lambda t: t + "\n// a note\n/* and\n more */\n")) == base
+    assert bench.kernel_source_digest(lambda r: read(r, lambda t: t.replace("kThreads", "kThreads ", 1))) == base
+    assert bench.kernel_source_digest(lambda r: read(r, lambda t: t + "\nstatic int x;\n")) != base
