@@ -16,10 +16,6 @@
 namespace lioncub {
 hipError_t launch_step(const StepParams& p, int nblk, int theta_bf16, int grad_bf16, int agg,
                        hipStream_t st);
-hipError_t launch_step_split(const StepParams& p, int nblk, int theta_bf16, int grad_bf16, int agg,
-                             uint64_t* wbits, hipStream_t st);
-hipError_t launch_apply_split(const StepParams& p, int nblk, int theta_bf16, int grad_bf16,
-                              hipStream_t st);
 hipError_t launch_zero_tail_words(uint64_t* bits, int64_t words, int64_t first, int W,
                                   hipStream_t st);
 hipError_t launch_stats_reduce(const StepParams& p, int nT, hipStream_t st);
@@ -50,14 +46,12 @@ namespace {
 constexpr size_t kWsAlign = 256;
 
 struct WsLayout {
-  size_t blk, tens, grp, partial, gval, m1, scale, bstat, gstat, wbits, total;
+  size_t blk, tens, grp, partial, gval, m1, scale, bstat, gstat, total;
 };
 
 size_t align_up(size_t x) { return (x + kWsAlign - 1) / kWsAlign * kWsAlign; }
 
-// wbits: the two-kernel 1-bit step's bitmaps [W][ld/64] (large vote and
-// averaging configurations only, see one_bit).
-WsLayout ws_layout(int64_t nblk, int64_t ngrp, int64_t nT, int64_t W, int64_t ld, bool one_bit) {
+WsLayout ws_layout(int64_t nblk, int64_t ngrp, int64_t nT, int64_t W) {
   WsLayout L;
   size_t o = 0;
   L.blk = o;
@@ -78,8 +72,6 @@ WsLayout ws_layout(int64_t nblk, int64_t ngrp, int64_t nT, int64_t W, int64_t ld
   o = align_up(o + static_cast<size_t>(nblk) * kStat * sizeof(uint64_t));
   L.gstat = o;
   o = align_up(o + static_cast<size_t>(ngrp) * kStat * sizeof(uint64_t));
-  L.wbits = o;
-  o = align_up(o + (one_bit ? static_cast<size_t>(W) * static_cast<size_t>(ld / 64) * 8 : 0));
   L.total = o;
   return L;
 }
@@ -123,23 +115,6 @@ int check_config(const lioncub_config* c, int64_t* nblk, int64_t* ngrp) {
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-// The two-kernel 1-bit step (vote and averaging paths) pays for its bitmap
-// round trip only on large states: timed in one process against the fused
-// kernel it was 4% faster at 350M x 16 and 2.5% at 124M x 8, but 2% slower
-// at 64M x 8 and up to 50% slower on cache-resident vectors.  It is used
-// from W * ld >= 3 * 2^28 worker-elements (m of 3 GiB) up.
-constexpr int64_t kSplitFrom = int64_t{3} << 28;
-
-// lioncub_apply's two kernels (momentum, then theta) add no bytes and pay
-// from W * ld >= 2^28 up (5.5% faster at 64M x 8, 7% at 350M x 16; slower on
-// cache-resident states).
-constexpr int64_t kApplySplitFrom = int64_t{1} << 28;
-
-bool one_bit(const lioncub_config* c) {
-  return (c->agg == LIONCUB_AGG_VOTE || c->agg == LIONCUB_AGG_AVG) &&
-         static_cast<int64_t>(c->W) * c->ld >= kSplitFrom;
-}
-
 }  // namespace
 
 struct lioncub_ctx {
@@ -157,7 +132,6 @@ struct lioncub_ctx {
   double* scale;
   uint64_t* bstat;
   uint64_t* gstat;
-  uint64_t* wbits;  // null unless the configuration is on a 1-bit path
   std::vector<BlockEnt> h_blk;
   std::vector<TensorEnt> h_tens;
   std::vector<GroupEnt> h_grp;
@@ -243,7 +217,7 @@ extern "C" {
 size_t lioncub_workspace_bytes(const lioncub_config* cfg) {
   int64_t nblk = 0, ngrp = 0;
   if (check_config(cfg, &nblk, &ngrp) != LIONCUB_OK) return 0;
-  return ws_layout(nblk, ngrp, cfg->n_tensors, cfg->W, cfg->ld, one_bit(cfg)).total;
+  return ws_layout(nblk, ngrp, cfg->n_tensors, cfg->W).total;
 }
 
 int lioncub_init(lioncub_ctx** out, const lioncub_config* cfg, void* hip_stream, void* workspace,
@@ -253,7 +227,7 @@ int lioncub_init(lioncub_ctx** out, const lioncub_config* cfg, void* hip_stream,
   int64_t nblk = 0, ngrp = 0;
   int st = check_config(cfg, &nblk, &ngrp);
   if (st != LIONCUB_OK) return st;
-  const WsLayout L = ws_layout(nblk, ngrp, cfg->n_tensors, cfg->W, cfg->ld, one_bit(cfg));
+  const WsLayout L = ws_layout(nblk, ngrp, cfg->n_tensors, cfg->W);
   if (!workspace || !aligned(workspace, kWsAlign) || ws_bytes < L.total) return LIONCUB_EWORKSPACE;
 
   lioncub_ctx* c = new (std::nothrow) lioncub_ctx();
@@ -272,7 +246,6 @@ int lioncub_init(lioncub_ctx** out, const lioncub_config* cfg, void* hip_stream,
   c->scale = reinterpret_cast<double*>(ws + L.scale);
   c->bstat = reinterpret_cast<uint64_t*>(ws + L.bstat);
   c->gstat = reinterpret_cast<uint64_t*>(ws + L.gstat);
-  c->wbits = one_bit(cfg) ? reinterpret_cast<uint64_t*>(ws + L.wbits) : nullptr;
 
   // the host tables are sized once, so nothing below can throw
   try {
@@ -383,15 +356,8 @@ int lioncub_step(lioncub_ctx* ctx, void* theta, float* m, const void* g, int64_t
     if (e == hipSuccess)
       e = run(ctx, LIONCUB_K_M1_FINALIZE, [&] { return launch_m1_finalize(q, linf, ctx->stream); });
   }
-  // The 1-bit paths run as two kernels (pack with the momentum update, then
-  // vote and theta) except when a debug output is asked for or this step
-  // averages momenta (the mean needs every worker's m' in one workgroup).
-  const bool split = ctx->wbits && !dbg && !(p.avg_step && ctx->any_sync);
   if (e == hipSuccess)
     e = run(ctx, kind, [&] {
-      if (split)
-        return launch_step_split(p, ctx->nblk, cf.theta_dtype, cf.grad_dtype, agg, ctx->wbits,
-                                 ctx->stream);
       return launch_step(p, ctx->nblk, cf.theta_dtype, cf.grad_dtype, agg, ctx->stream);
     });
   if (e == hipSuccess && p.bits)
@@ -430,10 +396,7 @@ int lioncub_apply(lioncub_ctx* ctx, void* theta, float* m, const void* g, int64_
   p.avg_step = (t % cf.sync_every) == 0;
   p.sign_bits = sign_bits;
   p.zero_bits = zero_bits;
-  const bool split = static_cast<int64_t>(cf.W) * cf.ld >= kApplySplitFrom &&
-                     !(p.avg_step && ctx->any_sync);
   return dev_status(run(ctx, LIONCUB_K_APPLY, [&] {
-    if (split) return launch_apply_split(p, ctx->nblk, cf.theta_dtype, cf.grad_dtype, ctx->stream);
     return launch_step(p, ctx->nblk, cf.theta_dtype, cf.grad_dtype, kAggApply, ctx->stream);
   }));
 }

@@ -27,12 +27,7 @@
 // stores follow.  HBM-bound: per element it moves W*(4 + s_g + 4) + 2*s_theta
 // bytes on every path -- nothing else (the quantised paths' norm pass is a
 // separate kernel).
-//
-// Two pairs of kernels at the end of the file split the work differently for
-// large states, because workgroups that stream a single worker row run
-// faster than ones that walk all W rows: the 1-bit step as "sign bits and
-// momentum per (block, worker)" then "vote and theta", and lioncub_apply as
-// "momentum per (block, worker)" then "theta from the planes".
+
 #include "device.hpp"
 #include "layout.hpp"
 
@@ -472,235 +467,6 @@ hipError_t launch_step(const StepParams& p, int nblk, int theta_bf16, int grad_b
   }
 }
 
-
-// ---------------------------------------------------------------------------
-// The 1-bit step in two kernels (vote and D-Lion averaging, production calls
-// on steps without momentum averaging).  They are the two halves of the
-// worker-sharded exchange run back to back: every worker packs the signs of
-// its c and updates its own momentum (k_vote_packm, one workgroup per (block,
-// worker)); then the receive side counts the W bitmaps and updates theta
-// (k_vote_theta, one workgroup per block).  The bitmaps make a round trip
-// through the workspace (W/4 bytes per parameter on top of the fused step's
-// W*(8 + s_g) + 2*s_theta), and still the pair is ~4% faster than the fused
-// kernel on 350M x 16 and 124M x 8 (same-process timing, bit-identical
-// theta and m): workgroups that stream one worker row each reach a higher
-// rate than workgroups that walk all W rows (see the fused kernel above).
-
-// One workgroup per (block, worker), grid (nblk, W): c, its sign bit (zeros by
-// the step parity) and m' of the thread's four quads; the 64 words of the
-// block go through LDS and leave as one nontemporal run.
-template <int GT>
-__global__ __launch_bounds__(kThreads) void k_vote_packm(StepParams p, uint64_t* __restrict__ wbits) {
-  __shared__ uint64_t sh[kBlock / 64];
-  const BlockEnt be = block_of(p.blk, p.flat, p.d);
-  const int64_t i = blockIdx.y;
-  const int tid = threadIdx.x;
-  const uint32_t par = static_cast<uint32_t>(p.parity);
-  F4 mv[kRounds], gv[kRounds];
-  int nv[kRounds];
-#pragma unroll
-  for (int q = 0; q < kRounds; ++q) {
-    const int loc = kThreads * kQuad * q + kQuad * tid;
-    nv[q] = max(0, min(kQuad, be.len - loc));
-    const int64_t idx = i * p.ld + be.start + loc;
-    if (nv[q] > 0) {
-      mv[q] = ldnt_f32x4(p.m + idx, nv[q]);
-      gv[q] = ldnt_x4<GT>(p.g, idx, nv[q]);
-    } else {
-#pragma unroll
-      for (int k = 0; k < 4; ++k) mv[q].v[k] = gv[q].v[k] = 0.0f;
-    }
-  }
-#pragma unroll
-  for (int q = 0; q < kRounds; ++q) {
-    const int loc = kThreads * kQuad * q + kQuad * tid;
-    const int64_t idx = i * p.ld + be.start + loc;
-    uint32_t nib = 0;
-    F4 mn;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const float c = (p.beta1 * mv[q].v[k]) + (p.omega1 * gv[q].v[k]);
-      nib |= (k < nv[q] ? sign_bit(c, par) : 0u) << k;
-      mn.v[k] = (p.beta2 * mv[q].v[k]) + (p.omega2 * gv[q].v[k]);
-    }
-    if (nv[q] > 0) stnt_f32x4(p.m + idx, mn, nv[q]);
-    const uint64_t word = row_pack_word(nib);  // every lane takes part
-    if ((tid & 15) == 15) sh[loc >> 6] = word;
-  }
-  __syncthreads();
-  // block starts are multiples of 64, so word tid of the block exists iff its
-  // first element does
-  if (tid < kBlock / 64 && 64 * tid < be.len)
-    stnt_u64(wbits + i * (p.ld >> 6) + (be.start >> 6) + tid, sh[tid]);
-}
-
-// One workgroup per block: the block's words of 16 workers at a time are
-// staged in LDS (coalesced 512-byte rows), each thread counts the +1 bits
-// of its quads in byte lanes, then the vote (or the D-Lion mean) updates
-// theta exactly as the fused kernel does.
-template <int TT, int AGG>
-__global__ __launch_bounds__(kThreads) void k_vote_theta(StepParams p,
-                                                         const uint64_t* __restrict__ wbits) {
-  __shared__ uint64_t sh[16][kBlock / 64];
-  const BlockEnt be = block_of(p.blk, p.flat, p.d);
-  const int tid = threadIdx.x;
-  const int W = p.W;
-  const int nw = (be.len + 63) >> 6;
-  const int64_t w0 = be.start >> 6, words = p.ld >> 6;
-  uint32_t cnt[kRounds] = {0u, 0u, 0u, 0u};
-  for (int i0 = 0; i0 < W; i0 += 16) {  // uniform
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int slot = r * kThreads + tid, ii = slot >> 6, w = slot & 63;
-      sh[ii][w] = (i0 + ii < W && w < nw)
-                      ? __builtin_nontemporal_load(wbits + static_cast<int64_t>(i0 + ii) * words + w0 + w)
-                      : 0ull;
-    }
-    __syncthreads();
-    const int nn = min(16, W - i0);
-#pragma unroll
-    for (int q = 0; q < kRounds; ++q) {
-      const int loc = kThreads * kQuad * q + kQuad * tid;
-      for (int ii = 0; ii < nn; ++ii)
-        cnt[q] += nibble_to_bytes(static_cast<uint32_t>(sh[ii][loc >> 6] >> (loc & 63)) & 0xFu);
-    }
-    __syncthreads();
-  }
-  const uint32_t par = static_cast<uint32_t>(p.parity);
-#pragma unroll
-  for (int q = 0; q < kRounds; ++q) {
-    const int loc = kThreads * kQuad * q + kQuad * tid;
-    const int nvq = max(0, min(kQuad, be.len - loc));
-    if (nvq == 0) continue;
-    const int64_t j = be.start + loc;
-    F4 th = ld_x4<TT>(p.theta, j, nvq);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int v = static_cast<int>((cnt[q] >> (8 * k)) & 0xFFu);
-      float sf;
-      if constexpr (AGG == kAggVote) {
-        const int twice = 2 * v;
-        sf = static_cast<float>(twice > W ? 1 : (twice < W ? -1 : (p.tie_zero ? 0 : (par ? 1 : -1))));
-      } else {
-        sf = static_cast<float>(2 * v - W) / static_cast<float>(W);
-      }
-      const float x = th.v[k];
-      th.v[k] = x - (p.lr * (sf + (p.wd * x)));
-    }
-    stnt_x4<TT>(p.theta, j, th, nvq);
-  }
-}
-
-template <int TT, int GT, int AGG>
-static hipError_t launch_split_t(const StepParams& p, int nblk, uint64_t* wbits, hipStream_t st) {
-  hipLaunchKernelGGL(k_vote_packm<GT>, dim3(nblk, p.W), dim3(kThreads), 0, st, p, wbits);
-  const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_vote_theta<TT, AGG>), dim3(nblk), dim3(kThreads), 0, st, p,
-                     static_cast<const uint64_t*>(wbits));
-  return hipGetLastError();
-}
-
-hipError_t launch_step_split(const StepParams& p, int nblk, int theta_bf16, int grad_bf16, int agg,
-                             uint64_t* wbits, hipStream_t st) {
-  const int key = (theta_bf16 << 2) | (grad_bf16 << 1) | (agg == kAggAvg ? 1 : 0);
-  if (agg != kAggVote && agg != kAggAvg) return hipErrorInvalidValue;
-  switch (key) {
-    case 0: return launch_split_t<0, 0, kAggVote>(p, nblk, wbits, st);
-    case 1: return launch_split_t<0, 0, kAggAvg>(p, nblk, wbits, st);
-    case 2: return launch_split_t<0, 1, kAggVote>(p, nblk, wbits, st);
-    case 3: return launch_split_t<0, 1, kAggAvg>(p, nblk, wbits, st);
-    case 4: return launch_split_t<1, 0, kAggVote>(p, nblk, wbits, st);
-    case 5: return launch_split_t<1, 0, kAggAvg>(p, nblk, wbits, st);
-    case 6: return launch_split_t<1, 1, kAggVote>(p, nblk, wbits, st);
-    default: return launch_split_t<1, 1, kAggAvg>(p, nblk, wbits, st);
-  }
-}
-
-
-// ---------------------------------------------------------------------------
-// lioncub_apply as two kernels on large states.  m' does not depend on the
-// global sign, so the momentum update runs with one workgroup per (block,
-// worker) -- the access pattern that streams fastest here -- and a second
-// kernel updates theta from the sign planes; no byte is added.  Timed in one
-// process against the fused apply mode: 12.25-12.27 vs 13.12-13.22 ms on
-// 350M x 16, 1.16 vs 1.22-1.23 ms on 64M x 8; slower only on cache-resident
-// states (16M x 8 and below), where the second launch costs more than the
-// pattern gains.  Steps that average momenta keep the fused kernel.
-
-template <int GT>
-__global__ __launch_bounds__(kThreads) void k_momentum(StepParams p) {
-  const BlockEnt be = block_of(p.blk, p.flat, p.d);
-  const int64_t i = blockIdx.y;
-  const int tid = threadIdx.x;
-  F4 mv[kRounds], gv[kRounds];
-  int nv[kRounds];
-#pragma unroll
-  for (int q = 0; q < kRounds; ++q) {
-    const int loc = kThreads * kQuad * q + kQuad * tid;
-    nv[q] = max(0, min(kQuad, be.len - loc));
-    const int64_t idx = i * p.ld + be.start + loc;
-    if (nv[q] > 0) {
-      mv[q] = ldnt_f32x4(p.m + idx, nv[q]);
-      gv[q] = ldnt_x4<GT>(p.g, idx, nv[q]);
-    }
-  }
-#pragma unroll
-  for (int q = 0; q < kRounds; ++q) {
-    if (nv[q] == 0) continue;
-    const int64_t idx = i * p.ld + be.start + kThreads * kQuad * q + kQuad * tid;
-    F4 mn;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) mn.v[k] = (p.beta2 * mv[q].v[k]) + (p.omega2 * gv[q].v[k]);
-    stnt_f32x4(p.m + idx, mn, nv[q]);
-  }
-}
-
-// theta from the sign planes (16 lanes share a plane word), as the fused
-// apply mode computes it.
-template <int TT>
-__global__ __launch_bounds__(kThreads) void k_theta_planes(StepParams p) {
-  const BlockEnt be = block_of(p.blk, p.flat, p.d);
-  const int tid = threadIdx.x;
-#pragma unroll
-  for (int q = 0; q < kRounds; ++q) {
-    const int loc = kThreads * kQuad * q + kQuad * tid;
-    const int nvq = max(0, min(kQuad, be.len - loc));
-    if (nvq == 0) continue;
-    const int64_t j = be.start + loc;
-    const int sh = static_cast<int>(j & 63);
-    const uint32_t pos = static_cast<uint32_t>(p.sign_bits[j >> 6] >> sh) & 0xFu;
-    const uint32_t zer =
-        p.zero_bits ? static_cast<uint32_t>(p.zero_bits[j >> 6] >> sh) & 0xFu : 0u;
-    F4 th = ld_x4<TT>(p.theta, j, nvq);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const float sf = static_cast<float>(((zer >> k) & 1u) ? 0 : (((pos >> k) & 1u) ? 1 : -1));
-      const float x = th.v[k];
-      th.v[k] = x - (p.lr * (sf + (p.wd * x)));
-    }
-    stnt_x4<TT>(p.theta, j, th, nvq);
-  }
-}
-
-template <int TT, int GT>
-static hipError_t launch_apply_split_t(const StepParams& p, int nblk, hipStream_t st) {
-  hipLaunchKernelGGL(k_momentum<GT>, dim3(nblk, p.W), dim3(kThreads), 0, st, p);
-  const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_theta_planes<TT>, dim3(nblk), dim3(kThreads), 0, st, p);
-  return hipGetLastError();
-}
-
-hipError_t launch_apply_split(const StepParams& p, int nblk, int theta_bf16, int grad_bf16,
-                              hipStream_t st) {
-  switch ((theta_bf16 << 1) | grad_bf16) {
-    case 0: return launch_apply_split_t<0, 0>(p, nblk, st);
-    case 1: return launch_apply_split_t<0, 1>(p, nblk, st);
-    case 2: return launch_apply_split_t<1, 0>(p, nblk, st);
-    default: return launch_apply_split_t<1, 1>(p, nblk, st);
-  }
-}
 
 hipError_t launch_zero_tail_words(uint64_t* bits, int64_t words, int64_t first, int W,
                                   hipStream_t st) {

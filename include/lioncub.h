@@ -129,8 +129,7 @@ typedef struct {
 
 /* Bytes of device workspace lioncub_init needs for cfg (0 if cfg is invalid):
  * the block, tensor and group tables, the norm partials and scales, the
- * diagnostics' counters and, on the vote and averaging paths with
- * W*ld >= 3*2^28, W*ld/8 bytes of sign bitmaps.  Pure host computation. */
+ * diagnostics' counters.  Pure host computation. */
 size_t lioncub_workspace_bytes(const lioncub_config *cfg);
 
 /* Validate cfg, lay out the caller's workspace (device, >= the bytes above,
@@ -154,14 +153,9 @@ int lioncub_set_stream(lioncub_ctx *ctx, void *hip_stream);
  *          paths, codes/sums/m1 on the quantised paths, sign and the
  *          diagnostics on all); an output of another path is an error
  *          (LIONCUB_EINVAL)
- * On states of W*ld >= 3*2^28 elements the vote and averaging paths run as
- * two kernels, the halves of the 1-bit exchange back to back: sign bits and
- * momentum update per (block, worker) into the workspace's bitmaps, then
- * the vote (or mean) and theta; on smaller states, with a debug output, or
- * on a step that averages momenta, as one fused kernel (the same results,
- * bit for bit).  The quantised paths are
- * three kernels (norm block partials, per-(worker, tensor) norm and scale,
- * then the fused quantise-sum-apply). */
+ * The vote and averaging paths are one kernel; the quantised paths are
+ * three (norm block partials, per-(worker, tensor) norm and scale, then the
+ * fused quantise-sum-apply). */
 int lioncub_step(lioncub_ctx *ctx, void *theta, float *m, const void *g, int64_t t,
                  const lioncub_debug *dbg);
 
@@ -226,9 +220,7 @@ int lioncub_vote_bits(lioncub_ctx *ctx, const uint64_t *bits, int64_t t,
  * writes them; zero_bits may be NULL = no zeros): theta <- theta - lr*(s +
  * wd*theta) with s = zero ? 0 : (sign ? +1 : -1), then every worker's
  * momentum update and the selective averaging, exactly as lioncub_step.
- * theta/m/g as in lioncub_step; sign_bits/zero_bits device [ld/64].  From
- * W*ld >= 2^28 up, on steps that do not average momenta, the momentum
- * update and the theta update run as two kernels (the same results). */
+ * theta/m/g as in lioncub_step; sign_bits/zero_bits device [ld/64]. */
 int lioncub_apply(lioncub_ctx *ctx, void *theta, float *m, const void *g, int64_t t,
                   const uint64_t *sign_bits, const uint64_t *zero_bits);
 

@@ -41,8 +41,7 @@ def cfg(**kw):
 
 def test_workspace_bytes_layout():
     # blocks: ceil(4096/4096) + ceil(5904/4096) = 3, one group of block
-    # partials per tensor; 256-byte aligned pieces; the 1-bit paths (vote,
-    # averaging) add the two-kernel step's bitmaps, W * ld/64 words
+    # partials per tensor; 256-byte aligned pieces
     c = cfg()
     n = _abi.lioncub_workspace_bytes(c)
     blk = 3 * 16
@@ -56,16 +55,6 @@ def test_workspace_bytes_layout():
     al = lambda x: (x + 255) // 256 * 256
     assert n == (al(blk) + al(tens) + al(grp) + al(part) + al(gval) + 2 * al(m1) + al(bstat)
                  + al(gstat))
-    # from W * ld >= 3 * 2^28 the vote and averaging paths add W * ld/64 bitmap words
-    d = 3 * 2 ** 26
-    big_vote = _abi.lioncub_workspace_bytes(cfg(d=d, ld=d, W=4, tensor_offsets=[0, d]))
-    big_l1 = _abi.lioncub_workspace_bytes(cfg(d=d, ld=d, W=4, tensor_offsets=[0, d],
-                                              agg=_abi.AGG_L1SUM, qbits=4))
-    assert big_vote - big_l1 == al(4 * (d // 64) * 8)
-    below = _abi.lioncub_workspace_bytes(cfg(d=d - 64, ld=d - 64, W=4, tensor_offsets=[0, d - 64]))
-    below_l1 = _abi.lioncub_workspace_bytes(cfg(d=d - 64, ld=d - 64, W=4, tensor_offsets=[0, d - 64],
-                                                agg=_abi.AGG_L1SUM, qbits=4))
-    assert below == below_l1
     big = cfg(d=1_313_626_112, ld=1_313_626_112, W=8,
               tensor_offsets=[0, 1_000_000_000 // 64 * 64, 1_313_626_112])
     assert _abi.lioncub_workspace_bytes(big) > 0

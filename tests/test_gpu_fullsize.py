@@ -299,62 +299,36 @@ def test_entry_points_at_bench_size():
     torch.cuda.empty_cache()
 
 
-SPLIT_CASES = {
-    # W * ld just above 3 * 2^28: the vote and averaging paths take the
-    # two-kernel step (sign bits + momentum per (block, worker), then vote and
-    # theta); W > 16 exercises the receive side's 16-worker chunks
-    "vote-W255": wls.flat("split-vote-W255", 3_158_037, W=255, agg="vote", g_nu=3.0),
-    "avg-W40-bf16": wls.flat("split-avg-W40", 20_132_673, W=40, agg="avg", theta_dtype="bf16",
+LARGE_W_CASES = {
+    # many workers on states of ~6 GB: the fused step's generic worker loop
+    # (W not 4, 8 or 16) at full scale, a tie-zero vote over three tensors
+    "vote-W255": wls.flat("large-vote-W255", 3_158_037, W=255, agg="vote", g_nu=3.0),
+    "avg-W40-bf16": wls.flat("large-avg-W40", 20_132_673, W=40, agg="avg", theta_dtype="bf16",
                              grad_dtype="bf16", g_nu=3.0),
-    "vote-W17-tiezero-3T": wls.Workload(name="split-vote-W17",
+    "vote-W17-tiezero-3T": wls.Workload(name="large-vote-W17",
                                         tensors=[("a", 20_000_064), ("b", 4160), ("c", 27_380_000)],
                                         W=17, agg="vote", tie="zero", theta_dtype="bf16",
                                         g_nu=3.0),
 }
 
 
-@pytest.mark.parametrize("name", sorted(SPLIT_CASES))
-def test_two_kernel_one_bit_step(name):
-    """Above the size where the 1-bit paths run as two kernels: two
-    production steps against the oracle on sampled ranges, then one step
-    from the same state through the split kernels (production call) and
-    through the fused kernel (a debug output forces it): theta and m bit for
-    bit equal."""
-    import torch
-    wl = SPLIT_CASES[name]
-    assert wl.W * wl.ld >= 3 * 2 ** 28
-    run_fullsize(wl, steps=[1, 2], n_random=2)
-    torch.cuda.set_device(0)
-    lc = lioncub_for(wl)
-    theta = gen.device_theta(wl)
-    m = gen.device_m(wl)
-    g = gen.device_g(wl, 3)
-    thB, mB = theta.clone(), m.clone()
-    lc.step(theta, m, g, 3)                                          # two kernels
-    lc.step(thB, mB, g, 3, {"sign": torch.empty(wl.d, dtype=torch.int8, device="cuda")})
-    torch.cuda.synchronize()
-    assert torch.equal(theta.view(torch.int16) if wl.theta_dtype == "bf16" else theta,
-                       thB.view(torch.int16) if wl.theta_dtype == "bf16" else thB)
-    assert torch.equal(m, mB)
-    _say(name, "split == fused")
-    lc.close()
-    del theta, m, g, thB, mB
-    torch.cuda.empty_cache()
+@pytest.mark.parametrize("name", sorted(LARGE_W_CASES))
+def test_large_worker_counts(name):
+    """Two production steps with many workers on multi-gigabyte states,
+    against the oracle on sampled ranges."""
+    run_fullsize(LARGE_W_CASES[name], steps=[1, 2], n_random=2)
 
 
 @pytest.mark.parametrize("dtypes", [("f32", "f32"), ("bf16", "bf16")])
-def test_two_kernel_apply(dtypes):
-    """lioncub_apply on a state above the size where it runs as two kernels
-    (momentum per (block, worker), then theta from the planes), two tensors
-    with a ragged end, random sign and zero planes: sampled ranges bit for
-    bit against the oracle; then an averaging step of a synced tensor (the
-    fused kernel) the same way."""
+def test_apply_large_state(dtypes):
+    """lioncub_apply on a 33.5M x 8 state of two tensors with a ragged end,
+    random sign and zero planes: sampled ranges bit for bit against the
+    oracle, on a plain step and on an averaging step of the synced tensor."""
     import torch
     th_dt, g_dt = dtypes
-    wl = wls.Workload(name="split-apply", tensors=[("a", 16_777_216), ("b", 16_777_216 + 4160)],
+    wl = wls.Workload(name="large-apply", tensors=[("a", 16_777_216), ("b", 16_777_216 + 4160)],
                       W=8, theta_dtype=th_dt, grad_dtype=g_dt, sync_names=("b",), sync_every=2,
                       g_nu=3.0)
-    assert wl.W * wl.ld >= 2 ** 28
     torch.cuda.set_device(0)
     lc = lioncub_for(wl)
     theta, m = gen.device_theta(wl), gen.device_m(wl)
@@ -385,7 +359,7 @@ def test_two_kernel_apply(dtypes):
                       to_host(zb[j0 // 64:(j1 + 63) // 64]).view(np.uint64))
             check_float_state(f"theta[{j0}:{j1}] t={t}", to_host(theta[j0:j1]), th, bf16=tb)
             check_float_state(f"m[:, {j0}:{j1}] t={t}", to_host(m[:, j0:j1]), mc)
-        _say("split apply", dtypes, "t", t, "ok")
+        _say("apply", dtypes, "t", t, "ok")
         del g
     lc.close()
     del theta, m, sb, zb

@@ -228,35 +228,3 @@ def test_capture_refuses_windows_that_would_not_replay_exactly():
     with pytest.raises(ValueError):
         li.capture(th, m, gs[:2], 1)                # max-norm draws depend on the full t
     li.close()
-
-
-def test_captured_window_of_two_kernel_steps():
-    """A state large enough for the two-kernel 1-bit step (W * ld >= 3 *
-    2^28), with an averaging tensor every 2 steps so the window mixes split
-    and fused steps: a captured window of 2 steps replayed twice equals 4
-    eager steps of a second context on a copy of the state, bit for bit."""
-    import torch
-    from synth import gen as sgen
-    wl = wls.Workload(name="cws", tensors=[("a", 101_000_000), ("b", 4096 + 64)], W=8, agg="vote",
-                      sync_names=("b",), sync_every=2)
-    assert wl.W * wl.ld >= 3 * 2 ** 28
-    theta, m = sgen.device_theta(wl), sgen.device_m(wl)
-    th2, m2 = theta.clone(), m.clone()
-    gs = [torch.empty((wl.W, wl.ld), device="cuda") for _ in range(2)]
-    lc = lioncub_for(wl)
-    eager = lioncub_for(wl)
-    graph = lc.capture(theta, m, gs, 3)
-    t = 3
-    for rep in range(2):
-        for k in range(2):
-            sgen.fill_device_g(wl, t + k, gs[k])
-        torch.cuda.synchronize()
-        graph.replay()
-        for k in range(2):
-            eager.step(th2, m2, gs[k], t + k)
-        torch.cuda.synchronize()
-        assert torch.equal(theta, th2) and torch.equal(m, m2), rep
-        t += 2
-    del graph
-    lc.close()
-    eager.close()
