@@ -44,6 +44,7 @@ using namespace lioncub;
 namespace {
 
 constexpr size_t kWsAlign = 256;
+constexpr int64_t kMaxLd = int64_t{1} << 40;
 
 struct WsLayout {
   size_t blk, tens, grp, partial, gval, m1, scale, bstat, gstat, total;
@@ -107,7 +108,9 @@ int check_config(const lioncub_config* c, int64_t* nblk, int64_t* ngrp) {
     nb += b;
     ng += (b + kGroup - 1) / kGroup;
   }
-  if (nb > 0x7FFFFFFF) return LIONCUB_EUNSUPPORTED;
+  // blocks index a 1-D grid; element offsets i*ld + j (and their byte
+  // offsets) must stay far inside int64
+  if (nb > 0x7FFFFFFF || c->ld > kMaxLd) return LIONCUB_EUNSUPPORTED;
   *nblk = nb;
   *ngrp = ng;
   return LIONCUB_OK;

@@ -73,7 +73,9 @@ enum { LIONCUB_TIE_PARITY = 0, LIONCUB_TIE_ZERO = 1 };
 
 typedef struct {
   int64_t d;                     /* parameters per worker, >= 1                  */
-  int64_t ld;                    /* row stride of [W][ld] buffers, >= d, % 64 == 0 */
+  int64_t ld;                    /* row stride of [W][ld] buffers, >= d, % 64 == 0;
+                                    above 2^40 (or more than 2^31-1 blocks of
+                                    4096 per tensor summed) LIONCUB_EUNSUPPORTED */
   int32_t W;                     /* workers, 1..255                              */
   int32_t n_tensors;             /* tensors in the flat vector, >= 1             */
   const int64_t *tensor_offsets; /* HOST, n_tensors+1: off[0]=0 < off[1] < ... <

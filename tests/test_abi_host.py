@@ -86,6 +86,21 @@ def test_invalid_config_rejected_before_device(bad):
     assert not ctx.value
 
 
+@pytest.mark.parametrize("big", [
+    dict(ld=2**40 + 64),                                          # row stride
+    dict(d=2**40 + 64, ld=2**40 + 64, tensor_offsets=[0, 2**40 + 64]),
+])
+def test_unsupported_sizes_rejected_before_device(big):
+    c = cfg(**big)
+    assert _abi.lioncub_workspace_bytes(c) == 0
+    ctx = C.c_void_p()
+    st = _abi.lib().lioncub_init(C.byref(ctx), C.byref(c), None, C.c_void_p(256), 1 << 30)
+    assert st == _abi.EUNSUPPORTED
+    assert not ctx.value
+    ok = cfg(d=2**40, ld=2**40, tensor_offsets=[0, 2**40])
+    assert _abi.lioncub_workspace_bytes(ok) > 0
+
+
 def test_workspace_checked_before_device():
     c = cfg()
     n = _abi.lioncub_workspace_bytes(c)
