@@ -38,6 +38,11 @@ class LionCub:
         aggs = {"vote": AGG_VOTE, "l1": AGG_L1SUM, "avg": AGG_AVG, "linf": AGG_LINFSUM}
         if agg not in aggs:
             raise ValueError(f"agg must be one of {sorted(aggs)}, got {agg!r}")
+        for name, val, allowed in (("theta_dtype", theta_dtype, ("f32", "bf16")),
+                                   ("grad_dtype", grad_dtype, ("f32", "bf16")),
+                                   ("tie", tie, ("parity", "zero"))):
+            if val not in allowed:
+                raise ValueError(f"{name} must be one of {allowed}, got {val!r}")
         ld = ld if ld is not None else (d + 63) // 64 * 64
         offs = tensor_offsets if tensor_offsets is not None else [0, d]
         self.cfg = make_config(

@@ -81,3 +81,11 @@ def test_device_must_match():
     th, m, g = good_state()
     with pytest.raises(ValueError):
         _checks.step(S, torch.device("cuda", 0), th, m, g, None)
+
+
+@pytest.mark.parametrize("kw", [dict(theta_dtype="fp16"), dict(grad_dtype="f16"),
+                                dict(tie="even"), dict(agg="sum")])
+def test_lioncub_rejects_unknown_names_before_allocating(kw):
+    from communication_compressed_distributed_amd import LionCub
+    with pytest.raises(ValueError):
+        LionCub(d=4096, W=2, device="cpu", **kw)
