@@ -312,10 +312,8 @@ void lco_step_range(const lco_cfg *cfg, int64_t j0, int64_t j1,
       } else {
         int8_t q;
         if (cfg->agg == LCO_AGG_LINFSUM) {
-          uint64_t ctr = ((uint64_t)t * (uint64_t)W + (uint64_t)i) * (uint64_t)cfg->d +
-                         (uint64_t)j;
           q = lco_qinf(c, m1[(int64_t)i * cfg->n_tensors + T], cfg->qbits,
-                       lco_splitmix64(cfg->seed, ctr));
+                       lco_sr_u32(cfg->seed, cfg->d, W, t, i, j));
         } else {
           q = lco_q1(c, m1[(int64_t)i * cfg->n_tensors + T], cfg->qbits);
         }
@@ -387,6 +385,16 @@ uint64_t lco_splitmix64(uint64_t seed, uint64_t counter) {
   return z ^ (z >> 31);
 }
 
+/* The 32 random bits of element j of worker i at step t: the elements j and
+ * j + 1 (j even) share output number (t*W + i)*d + j of the stream, the even
+ * one taking its low 32 bits and the odd one its high 32 bits.  Counters
+ * wrap mod 2^64.  (A reading: the pages give no generator.) */
+uint32_t lco_sr_u32(uint64_t seed, int64_t d, int32_t W, int64_t t, int32_t i, int64_t j) {
+  uint64_t ctr = ((uint64_t)t * (uint64_t)W + (uint64_t)i) * (uint64_t)d + ((uint64_t)j & ~(uint64_t)1);
+  uint64_t r = lco_splitmix64(seed, ctr);
+  return (j & 1) ? (uint32_t)(r >> 32) : (uint32_t)r;
+}
+
 double lco_minf(const float *x, int64_t n) {
   double mx = 0.0;
   for (int64_t k = 0; k < n; k++) {
@@ -401,17 +409,17 @@ double lco_minf(const float *x, int64_t n) {
  * measured against; the pages name it but print no formula, so this is the
  * reading of Eq. (1) with max |x| for M1 and stochastic rounding:
  * floor(y) + [u < y - floor(y)], y = (2^(n-1)-1)/max|x| * x in fp64,
- * u = (draw >> 11) * 2^-53, clamped.  PARITY PARTLY UNPINNED (the formula is
- * a reading); pinned: integer y, the threshold's direction, the clamp,
- * unbiasedness and the pages' zero-collapse finding. */
-int8_t lco_qinf(float c, double minf, int32_t qbits, uint64_t draw) {
+ * u = r * 2^-32 for 32 random bits r (lco_sr_u32), clamped.  PARITY PARTLY
+ * UNPINNED (the formula is a reading); pinned: integer y, the threshold's
+ * direction, the clamp, unbiasedness and the pages' zero-collapse finding. */
+int8_t lco_qinf(float c, double minf, int32_t qbits, uint32_t r) {
   int32_t qmax = (1 << (qbits - 1)) - 1;
   if (minf == 0.0) return 0;
   double scale = (double)qmax / minf;
   double y = (double)c * scale;
   double fl = floor(y);
   double frac = y - fl;
-  double u = (double)(draw >> 11) * 0x1.0p-53;
+  double u = (double)r * 0x1.0p-32;
   double q = fl + (u < frac ? 1.0 : 0.0);
   if (q > (double)qmax) q = (double)qmax;
   if (q < -(double)qmax) q = -(double)qmax;
@@ -425,12 +433,9 @@ void lco_quant_linf(const lco_cfg *cfg, int64_t ld, const float *x, int64_t t,
       int64_t a = cfg->off[T], n = cfg->off[T + 1] - cfg->off[T];
       double M = lco_minf(x + i * ld + a, n);
       if (minf) minf[(int64_t)i * cfg->n_tensors + T] = M;
-      for (int64_t j = a; j < a + n; j++) {
-        uint64_t ctr = ((uint64_t)t * (uint64_t)cfg->W + (uint64_t)i) * (uint64_t)cfg->d +
-                       (uint64_t)j;
+      for (int64_t j = a; j < a + n; j++)
         codes[i * ld + j] = lco_qinf(x[i * ld + j], M, cfg->qbits,
-                                     lco_splitmix64(cfg->seed, ctr));
-      }
+                                     lco_sr_u32(cfg->seed, cfg->d, cfg->W, t, i, j));
     }
   }
 }

@@ -167,11 +167,16 @@ uint64_t lco_splitmix64(uint64_t seed, uint64_t counter);
 /* max |x| of one row of n values (exact: fp32 magnitudes, no rounding). */
 double lco_minf(const float *x, int64_t n);
 
-/* One stochastic code; `draw` is the generator output for this element. */
-int8_t lco_qinf(float c, double minf, int32_t qbits, uint64_t draw);
+/* The 32 random bits of element j of worker i at step t: output number
+ * (t*W + i)*d + (j with its lowest bit cleared) of the stream, its low 32
+ * bits for even j and its high 32 bits for odd j (counters mod 2^64). */
+uint32_t lco_sr_u32(uint64_t seed, int64_t d, int32_t W, int64_t t, int32_t i, int64_t j);
+
+/* One stochastic code, u = r * 2^-32 for the element's 32 random bits r. */
+int8_t lco_qinf(float c, double minf, int32_t qbits, uint32_t r);
 
 /* Standalone max-norm quantisation of x[W][ld] for step t: element j of
- * worker i uses the draw with counter (t*W + i)*d + j. */
+ * worker i uses lco_sr_u32(seed, d, W, t, i, j). */
 void lco_quant_linf(const lco_cfg *cfg, int64_t ld, const float *x, int64_t t,
                     int8_t *codes, double *minf);
 

@@ -76,7 +76,9 @@ def lib():
         L.lco_splitmix64.restype = C.c_uint64
         L.lco_minf.argtypes = [vp, i64]
         L.lco_minf.restype = C.c_double
-        L.lco_qinf.argtypes = [C.c_float, C.c_double, i32, C.c_uint64]
+        L.lco_sr_u32.argtypes = [C.c_uint64, i64, i32, i64, i32, i64]
+        L.lco_sr_u32.restype = C.c_uint32
+        L.lco_qinf.argtypes = [C.c_float, C.c_double, i32, C.c_uint32]
         L.lco_qinf.restype = C.c_int8
         L.lco_quant_linf.argtypes = [C.POINTER(Cfg), i64, vp, i64, vp, vp]
         L.lco_minf_all.argtypes = [C.POINTER(Cfg), i64, vp, vp, vp]
@@ -187,8 +189,14 @@ def minf(x):
     return lib().lco_minf(_p(x), x.size)
 
 
-def qinf(c, minf_v, qbits, draw):
-    return lib().lco_qinf(float(c), float(minf_v), int(qbits), int(draw) & (2**64 - 1))
+def sr_u32(seed, d, W, t, i, j):
+    """The 32 random bits of element j of worker i at step t."""
+    return lib().lco_sr_u32(int(seed) & (2**64 - 1), int(d), int(W), int(t), int(i), int(j))
+
+
+def qinf(c, minf_v, qbits, r):
+    """One max-norm stochastic code for the element's 32 random bits r."""
+    return lib().lco_qinf(float(c), float(minf_v), int(qbits), int(r) & (2**32 - 1))
 
 
 def quant_linf(wl, x, t):

@@ -261,9 +261,8 @@ def test_entry_points_at_bench_size():
             for k in range(2048):
                 j = j0 + k
                 assert cs[i, k] == lco.q1(xs[i, k], got_m1[i], n), (i, j, "q1")
-                ctr = (t * W + i) * d + j
-                draw = lco.splitmix64(wl.sr_seed, ctr)
-                assert ci[i, k] == lco.qinf(xs[i, k], got_minf[i], n, draw), (i, j, "qinf")
+                r = lco.sr_u32(wl.sr_seed, d, W, t, i, j)
+                assert ci[i, k] == lco.qinf(xs[i, k], got_minf[i], n, r), (i, j, "qinf")
         # wire format and the receive-side sum over the whole range
         want_wire = lco.pack_codes(cs, j1 - j0, n)
         g0, g1 = j0 // 32, j1 // 32

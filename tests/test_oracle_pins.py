@@ -725,7 +725,8 @@ def test_stats_momentum_variance_exact(oracle):
 # ----------------------------------- max-norm stochastic baseline (Q-inf) --
 # The pages name this quantiser as the baseline Eq. (1) replaces but do not
 # print it; the reading pinned here is Eq. (1) with max |x| in place of the
-# mean and stochastic rounding, u drawn by SplitMix64 keyed per element.
+# mean and stochastic rounding, u = r * 2^-32 for 32 bits r of a SplitMix64
+# output keyed per pair of elements.
 
 def test_splitmix64_published_outputs(oracle):
     """SplitMix64 (Steele, Lea, Flood 2014; Vigna's reference C version):
@@ -759,37 +760,43 @@ def test_qinf_integer_points_ignore_the_draw(oracle, n):
     M = _exact_minf(qmax)
     for k in range(-qmax, qmax + 1):
         c = float(Fraction(k, 2**10))
-        for draw in (0, 1 << 63, 2**64 - 1):
-            assert oracle.qinf(c, M, n, draw) == k
-    assert oracle.qinf(0.25, 0.0, n, 2**64 - 1) == 0      # all-zero row
+        for r in (0, 1 << 31, 2**32 - 1):
+            assert oracle.qinf(c, M, n, r) == k
+    assert oracle.qinf(0.25, 0.0, n, 2**32 - 1) == 0      # all-zero row
 
 
 def test_qinf_clamps_the_row_maximum(oracle):
     """x = +-max|x| where the fp64 product qmax/M * M rounds above qmax
-    (M = float32(0.0066045928), y = 7 + 2^-50): a draw of 0 would round up to
-    8, the clamp keeps +-qmax."""
+    (M = float32(0.0066045928), y = 7 + 2^-50): random bits 0 would round up
+    to 8, the clamp keeps +-qmax."""
     M = float(np.float32(0.006604592781513929))
     assert M * (7.0 / M) > 7.0
-    for draw in (0, 2**64 - 1):
-        assert oracle.qinf(M, M, 4, draw) == 7
-        assert oracle.qinf(-M, M, 4, draw) == -7
+    for r in (0, 2**32 - 1):
+        assert oracle.qinf(M, M, 4, r) == 7
+        assert oracle.qinf(-M, M, 4, r) == -7
 
 
 def test_qinf_draw_threshold_direction(oracle):
-    """y = 2.25: the code is 3 exactly when u = (draw >> 11) / 2^53 < 0.25
-    (probability 0.25 of rounding up), else 2; negatives round toward
-    floor(y) + 1 the same way."""
+    """y = 2.25: the code is 3 exactly when u = r / 2^32 < 0.25 (probability
+    0.25 of rounding up), else 2; negatives round toward floor(y) + 1 the
+    same way."""
     M = _exact_minf(7)
     c = float(Fraction(9, 4 * 2**10))                        # y = 2.25
-    at = (1 << 51) << 11                                     # u = 0.25
-    below = ((1 << 51) - 1) << 11                            # u = 0.25 - 2^-53
+    at = 1 << 30                                             # u = 0.25
+    below = (1 << 30) - 1                                    # u = 0.25 - 2^-32
     assert oracle.qinf(c, M, 4, below) == 3
     assert oracle.qinf(c, M, 4, at) == 2
     assert oracle.qinf(c, M, 4, 0) == 3
-    assert oracle.qinf(c, M, 4, 2**64 - 1) == 2
+    assert oracle.qinf(c, M, 4, 2**32 - 1) == 2
     # y = -2.25 = -3 + 0.75: up to -2 when u < 0.75
-    assert oracle.qinf(-c, M, 4, (3 << 51) - 1 << 11) == -2
-    assert oracle.qinf(-c, M, 4, (3 << 51) << 11) == -3
+    assert oracle.qinf(-c, M, 4, (3 << 30) - 1) == -2
+    assert oracle.qinf(-c, M, 4, 3 << 30) == -3
+    # a fraction finer than 2^-32: y = 2^-40 rounds up only for r = 0
+    c2 = 2.0**-50
+    assert oracle.qinf(c2, M, 4, 0) == 1 and oracle.qinf(c2, M, 4, 1) == 0
+    # -2^-40 = -1 + (1 - 2^-40): down to -1 needs u >= 1 - 2^-40, which no
+    # 32-bit r reaches (the rounding's bias is below 2^-32)
+    assert oracle.qinf(-c2, M, 4, 2**32 - 1) == 0 and oracle.qinf(-c2, M, 4, 0) == 0
 
 
 def test_qinf_unbiased_over_the_stream(oracle):
@@ -800,7 +807,8 @@ def test_qinf_unbiased_over_the_stream(oracle):
     for yq in (Fraction(13, 10), Fraction(-5, 8), Fraction(61, 10)):
         c = np.float32(float(yq / 2**10))
         y = Fraction(float(c)) * 2**10                       # the exact y
-        qs = np.array([oracle.qinf(float(c), M, 4, oracle.splitmix64(99, k)) for k in range(N)])
+        qs = np.array([oracle.qinf(float(c), M, 4, oracle.sr_u32(99, N, 1, 0, 0, k))
+                       for k in range(N)])
         fl = math.floor(y)
         assert set(np.unique(qs)) <= {fl, fl + 1}
         p = float(y - fl)
@@ -810,8 +818,9 @@ def test_qinf_unbiased_over_the_stream(oracle):
 
 def test_quant_linf_rows_and_counters(oracle):
     """Standalone codes: per (worker, tensor) max |x| exact; element j of
-    worker i at step t uses draw (t*W + i)*d + j of the seeded stream; the
-    dequantised codes are unbiased for x."""
+    worker i at step t takes the low (even j) or high (odd j) 32 bits of
+    output (t*W + i)*d + 2*floor(j/2) of the seeded stream; the dequantised
+    codes are unbiased for x."""
     wl = wls.Workload(name="qi", tensors=[("a", 4096 + 64), ("b", 192)], W=3, agg="linf",
                       qbits=4)
     rs = np.random.default_rng(8)
@@ -823,10 +832,12 @@ def test_quant_linf_rows_and_counters(oracle):
         for T in range(2):
             a, b = wl.offsets[T], wl.offsets[T + 1]
             assert mv[i, T] == float(np.max(np.abs(x[i, a:b])))
-    for i, j in ((0, 0), (2, 4100), (1, wl.d - 1)):
+    for i, j in ((0, 0), (0, 1), (2, 4100), (2, 4101), (1, wl.d - 1)):
         T = 0 if j < wl.offsets[1] else 1
-        draw = oracle.splitmix64(wl.sr_seed, (t * wl.W + i) * wl.d + j)
-        assert codes[i, j] == oracle.qinf(float(x[i, j]), mv[i, T], 4, draw)
+        r64 = oracle.splitmix64(wl.sr_seed, (t * wl.W + i) * wl.d + (j & ~1))
+        r = r64 >> 32 if j & 1 else r64 & 0xFFFFFFFF
+        assert oracle.sr_u32(wl.sr_seed, wl.d, wl.W, t, i, j) == r
+        assert codes[i, j] == oracle.qinf(float(x[i, j]), mv[i, T], 4, r)
     assert np.all(codes[:, wl.d:] == 0)
     # another step draws a different stream
     codes2, _ = oracle.quant_linf(wl, x, t + 1)
