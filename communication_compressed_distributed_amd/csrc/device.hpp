@@ -267,13 +267,22 @@ __device__ __forceinline__ uint64_t mix64(uint64_t z) {
   return z ^ (z >> 31);
 }
 
+// The 32 random bits of element k (0..3) of a quad whose first element is
+// even: the pair (k = 0, 1) shares draw r01 and the pair (2, 3) draw r23,
+// the even element taking the low half and the odd one the high half.
+__device__ __forceinline__ uint32_t quad_bits(uint64_t r01, uint64_t r23, int k) {
+  const uint64_t r = k < 2 ? r01 : r23;
+  return (k & 1) ? static_cast<uint32_t>(r >> 32) : static_cast<uint32_t>(r);
+}
+
 // Stochastic rounding of y = c * scale (fp64) onto the integers: floor(y) + 1
-// when u < y - floor(y), u = (draw >> 11) * 2^-53 uniform in [0, 1), else
-// floor(y); then clamped to +-qmax.  Every step is exact except the product.
-__device__ __forceinline__ int sr_code(float c, double scale, double qmax, uint64_t draw) {
+// when u < y - floor(y), u = r * 2^-32 uniform in [0, 1) for 32 random bits
+// r, else floor(y); then clamped to +-qmax.  Every step is exact except the
+// product.
+__device__ __forceinline__ int sr_code(float c, double scale, double qmax, uint32_t r) {
   const double y = static_cast<double>(c) * scale;
   const double fl = __builtin_floor(y);
-  const double u = static_cast<double>(draw >> 11) * 0x1.0p-53;
+  const double u = static_cast<double>(r) * 0x1.0p-32;
   double q = fl + (u < (y - fl) ? 1.0 : 0.0);
   q = fmin(fmax(q, -qmax), qmax);
   return static_cast<int>(q);

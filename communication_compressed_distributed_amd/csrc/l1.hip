@@ -21,8 +21,9 @@
 //
 // The max-norm baseline (MX = true) runs the same tree with max in place of
 // the sum and no division: a maximum is exact in any order.  Its codes round
-// stochastically (sr_code), with the SplitMix64 draw of element j of worker
-// i at step t taken at counter (t*W + i)*d + j.
+// stochastically (sr_code): element j of worker i at step t takes 32 bits of
+// SplitMix64 output number (t*W + i)*d + (j with its lowest bit cleared), the
+// low half for even j and the high half for odd j.
 #include "device.hpp"
 #include "layout.hpp"
 
@@ -303,13 +304,15 @@ __global__ __launch_bounds__(kThreads) void k_quant_codes_sr(M1Params p, int8_t*
       const int64_t idx = static_cast<int64_t>(i) * p.ld + be.start + loc;
       const F4 x = ldnt_f32x4(p.x + idx, nv);
       uint32_t packed = 0;
-      // counter of element k: (t*W + i)*d + j, j = be.start + loc + k
+      // elements j, j+1 (j = be.start + loc + 0 or 2, even) share output
+      // number (t*W + i)*d + j of the stream
       const uint64_t z0 = p.seed + (static_cast<uint64_t>(
           (static_cast<uint64_t>(p.t) * static_cast<uint64_t>(p.W) + static_cast<uint64_t>(i)) *
               static_cast<uint64_t>(p.d) + static_cast<uint64_t>(be.start + loc)) + 1u) * kGamma;
+      const uint64_t r01 = mix64(z0), r23 = mix64(z0 + 2u * kGamma);
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const int qc = sr_code(x.v[k], s, qm, mix64(z0 + static_cast<uint64_t>(k) * kGamma));
+        const int qc = sr_code(x.v[k], s, qm, quad_bits(r01, r23, k));
         packed |= (static_cast<uint32_t>(qc) & 0xFFu) << (8 * k);
       }
       stnt_b4(codes + idx, packed, nv);

@@ -60,8 +60,8 @@ struct StepParams {
   int32_t flat;        // one tensor: block b starts at b*kBlock (no table load)
   int32_t any_sync;    // some tensor is averaged (else no tensor-table load)
   int64_t d;
-  // stochastic rounding (max-norm path): draw of element j of worker i is
-  // output (t*W + i)*d + j of the SplitMix64 stream keyed by seed
+  // stochastic rounding (max-norm path): element j of worker i takes 32 bits
+  // of output (t*W + i)*d + (j & ~1) of the SplitMix64 stream keyed by seed
   uint64_t seed;
   int64_t t;
   // global sign given as bit planes (apply mode): [ld/64] each, zero may be null

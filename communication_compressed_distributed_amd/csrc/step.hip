@@ -171,8 +171,10 @@ __device__ __forceinline__ void step_block(const StepParams& p, const BlockEnt& 
     j[q] = be.start + loc;
     nv[q] = FULL ? kQuad : max(0, min(kQuad, be.len - loc));
   }
-  // max-norm draws: element j of worker i takes mix64(seed + ((t*W + i)*d +
-  // j + 1) * gamma) = mix64(zrow_i + j*gamma), wrapping mod 2^64
+  // max-norm draws: the quad at j (a multiple of 4) of worker i takes outputs
+  // (t*W + i)*d + j and + j + 2 of the stream, mix64(seed + (n + 1) * gamma)
+  // = mix64(zrow_i + j*gamma) and mix64(zrow_i + (j + 2)*gamma), mod 2^64;
+  // each output gives its pair of elements 32 bits apiece
   uint64_t jg[AGG == kAggLinf ? Q : 1];
   if constexpr (AGG == kAggLinf) {
 #pragma unroll
@@ -254,6 +256,11 @@ __device__ __forceinline__ void step_block(const StepParams& p, const BlockEnt& 
         const int64_t idx = static_cast<int64_t>(i) * p.ld + j[q];
         F4 mn;
         uint32_t nib = 0;
+        uint64_t r01 = 0, r23 = 0;
+        if constexpr (AGG == kAggLinf) {
+          r01 = mix64(zrow + jg[q]);
+          r23 = mix64(zrow + jg[q] + 2u * kGamma);
+        }
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           const float c = (p.beta1 * mv[b][q].v[k]) + (p.omega1 * gv[b][q].v[k]);
@@ -262,8 +269,7 @@ __device__ __forceinline__ void step_block(const StepParams& p, const BlockEnt& 
           } else if (kQ) {
             int qc;
             if constexpr (AGG == kAggLinf) {
-              qc = sr_code(c, s_i, static_cast<double>(p.qmax),
-                           mix64(zrow + jg[q] + static_cast<uint64_t>(k) * kGamma));
+              qc = sr_code(c, s_i, static_cast<double>(p.qmax), quad_bits(r01, r23, k));
             } else {
               double y = __builtin_rint(static_cast<double>(c) * s_i);
               y = fmin(fmax(y, -static_cast<double>(p.qmax)), static_cast<double>(p.qmax));

@@ -189,9 +189,10 @@ int lioncub_quant_l1(lioncub_ctx *ctx, const float *x, int8_t *codes, double *m1
  * not printed there, this is the reading taken):
  *   q = clamp(floor(y) + [u < y - floor(y)], +-(2^(n-1)-1)),
  *   y = (2^(n-1)-1) / max|x| * x in fp64 (scale 0 when max|x| == 0),
- *   u = (r >> 11) * 2^-53, r = SplitMix64 output (t*W + i)*d + j of the
- *   stream keyed by cfg.sr_seed, i.e. mix(sr_seed + (counter+1)*0x9E3779B97F4A7C15)
- *   with Steele-Lea-Flood's mixer (shifts 30/27/31, multipliers
+ *   u = b * 2^-32, b = the low 32 bits (even j) or the high 32 bits (odd j)
+ *   of SplitMix64 output number (t*W + i)*d + (j & ~1) of the stream keyed
+ *   by cfg.sr_seed, i.e. mix(sr_seed + (number+1)*0x9E3779B97F4A7C15) with
+ *   Steele-Lea-Flood's mixer (shifts 30/27/31, multipliers
  *   0xBF58476D1CE4E5B9 and 0x94D049BB133111EB), all mod 2^64.
  * x[W][ld] (device fp32) -> codes[W][ld] (device int8, columns j >= d
  * untouched) and, if minf != NULL, minf[W][n_tensors] (device fp64) = max |x|
