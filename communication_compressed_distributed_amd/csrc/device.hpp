@@ -278,14 +278,14 @@ __device__ __forceinline__ uint32_t quad_bits(uint64_t r01, uint64_t r23, int k)
 // Stochastic rounding of y = c * scale (fp64) onto the integers: floor(y) + 1
 // when u < y - floor(y), u = r * 2^-32 uniform in [0, 1) for 32 random bits
 // r, else floor(y); then clamped to +-qmax.  Every step is exact except the
-// product.
-__device__ __forceinline__ int sr_code(float c, double scale, double qmax, uint32_t r) {
+// product; |c| <= max|c| keeps floor(y) within +-(qmax + 1), so the integer
+// form of the last two steps is exact.
+__device__ __forceinline__ int sr_code(float c, double scale, int qmax, uint32_t r) {
   const double y = static_cast<double>(c) * scale;
   const double fl = __builtin_floor(y);
   const double u = static_cast<double>(r) * 0x1.0p-32;
-  double q = fl + (u < (y - fl) ? 1.0 : 0.0);
-  q = fmin(fmax(q, -qmax), qmax);
-  return static_cast<int>(q);
+  const int q = static_cast<int>(fl) + (u < (y - fl) ? 1 : 0);
+  return min(max(q, -qmax), qmax);
 }
 
 }  // namespace lioncub

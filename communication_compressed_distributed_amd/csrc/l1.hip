@@ -257,7 +257,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_codes(M1Params p, int8_t* __
   const BlockEnt be = block_of(p.blk, p.flat, p.d);
   const int tid = threadIdx.x;
   const int i = blockIdx.y;
-  const double qm = static_cast<double>(p.qmax);
+  const int qm = p.qmax;
   const double s = p.scale[static_cast<int64_t>(i) * p.nT + be.tensor];
   const int64_t row = static_cast<int64_t>(i) * p.ld + be.start;
   F4 x[kRounds];
@@ -292,7 +292,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_codes(M1Params p, int8_t* __
 __global__ __launch_bounds__(kThreads) void k_quant_codes_sr(M1Params p, int8_t* __restrict__ codes) {
   const BlockEnt be = block_of(p.blk, p.flat, p.d);
   const int tid = threadIdx.x;
-  const double qm = static_cast<double>(p.qmax);
+  const int qm = p.qmax;
 #pragma unroll 1
   for (int i = 0; i < p.W; ++i) {
     const double s = p.scale[static_cast<int64_t>(i) * p.nT + be.tensor];

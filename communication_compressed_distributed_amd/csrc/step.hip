@@ -269,7 +269,7 @@ __device__ __forceinline__ void step_block(const StepParams& p, const BlockEnt& 
           } else if (kQ) {
             int qc;
             if constexpr (AGG == kAggLinf) {
-              qc = sr_code(c, s_i, static_cast<double>(p.qmax), quad_bits(r01, r23, k));
+              qc = sr_code(c, s_i, p.qmax, quad_bits(r01, r23, k));
             } else {
               double y = __builtin_rint(static_cast<double>(c) * s_i);
               y = fmin(fmax(y, -static_cast<double>(p.qmax)), static_cast<double>(p.qmax));

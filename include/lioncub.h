@@ -198,7 +198,8 @@ int lioncub_quant_l1(lioncub_ctx *ctx, const float *x, int8_t *codes, double *m1
  * untouched) and, if minf != NULL, minf[W][n_tensors] (device fp64) = max |x|
  * per (worker, tensor).  t >= 1 selects the draws (the fused step with
  * LIONCUB_AGG_LINFSUM at step t draws the same ones for c).  Needs qbits in
- * 2..8 in the config. */
+ * 2..8 in the config.  Codes of a row holding NaN or infinity are
+ * unspecified. */
 int lioncub_quant_linf(lioncub_ctx *ctx, const float *x, int64_t t, int8_t *codes,
                        double *minf);
 
