@@ -63,6 +63,12 @@ EDGE = {
     "W4-l1-generic-bf16g": wls.flat("e15", 3 * 4096 + 4, W=4, agg="l1", qbits=5,
                                     grad_dtype="bf16"),
     "W8-vote-f32-bf16theta": wls.flat("e16", 3 * 4096 + 8, W=8, theta_dtype="bf16"),
+    # 255 momenta summed in fp32 in worker order for the synced tensor, every step
+    "W255-l1q8-sync": wls.Workload(name="e17", tensors=[("wte", 640), ("h", 384)], W=255,
+                                   agg="l1", qbits=8, sync_names=("wte",), sync_every=1),
+    "W255-vote-bf16-sync": wls.Workload(name="e18", tensors=[("h", 4096 + 64), ("wpe", 128)],
+                                        W=255, theta_dtype="bf16", grad_dtype="bf16",
+                                        sync_names=("wpe",), sync_every=1),
 }
 
 
@@ -280,6 +286,8 @@ AVG = {
     "avg-W16-sync": wls.Workload(name="a3", tensors=[("wte", 4096 + 64), ("h", 8192)], W=16,
                                  agg="avg", sync_names=("wte",), sync_every=2),
     "avg-W8-gpt": small(wls.GPT2_124M_W8_VOTE.with_(agg="avg"), 4096 + 640, 20),
+    "avg-W255-sync": wls.Workload(name="a5", tensors=[("wte", 640), ("h", 4096 + 64)], W=255,
+                                  agg="avg", sync_names=("wte",), sync_every=1),
 }
 
 
