@@ -69,6 +69,13 @@ EDGE = {
     "W255-vote-bf16-sync": wls.Workload(name="e18", tensors=[("h", 4096 + 64), ("wpe", 128)],
                                         W=255, theta_dtype="bf16", grad_dtype="bf16",
                                         sync_names=("wpe",), sync_every=1),
+    # padded rows with bf16 data and several tensors
+    "row-padding-bf16-l1-tensors": wls.Workload(name="e19", tensors=[("a", 4096 + 192), ("b", 320)],
+                                                W=6, agg="l1", qbits=6, theta_dtype="bf16",
+                                                grad_dtype="bf16", ld_pad=256),
+    "row-padding-bf16g-avg-sync": wls.Workload(name="e20", tensors=[("wte", 192), ("h", 4096 + 5)],
+                                               W=5, agg="avg", grad_dtype="bf16", ld_pad=64,
+                                               sync_names=("wte",), sync_every=3),
 }
 
 
