@@ -65,7 +65,9 @@ def check_float_state(name, got, want, bf16=False):
 def inject_zeros(wl, m, g, rs, frac=0.01):
     """Zero m and g at random (worker, element) spots so that c is exactly 0
     there (the parity rule), and all workers of some columns (ties at every
-    W), and one whole (worker, tensor) row on the quantised paths (norm 0)."""
+    W), and one whole (worker, tensor) row on the quantised paths (norm 0).
+    Applies them to the host arrays and returns the positions, so the same
+    zeros can be written into the device momentum without copying state."""
     d = wl.d
     mask = rs.random((wl.W, d)) < frac
     m[:, :d][mask] = 0
@@ -73,15 +75,34 @@ def inject_zeros(wl, m, g, rs, frac=0.01):
     cols = rs.integers(0, d, max(1, d // 200))
     m[:, cols] = 0
     g[:, cols] = 0
+    row = None
     if wl.agg in ("l1", "linf") and wl.n_tensors > 1:
         a, b = wl.offsets[1], wl.offsets[2]
         m[wl.W - 1, a:b] = 0
         g[wl.W - 1, a:b] = 0
+        row = (wl.W - 1, a, b)
+    return mask, cols, row
+
+
+def zero_device_m(d_m, wl, zeros):
+    """Write the zeros inject_zeros chose into the device momentum in place:
+    the device keeps its own trajectory (nothing of the oracle's state is
+    copied over), only the same inputs are perturbed on both sides."""
+    import torch
+    mask, cols, row = zeros
+    view = d_m[:, : wl.d]
+    view[torch.from_numpy(mask).to(d_m.device)] = 0
+    d_m[:, torch.from_numpy(cols).to(d_m.device)] = 0
+    if row is not None:
+        i, a, b = row
+        d_m[i, a:b] = 0
 
 
 def gpu_step_vs_oracle(wl, steps=2, t0=1, zeros=True, debug=True, seed_shift=0):
     """Run `steps` steps on both sides from the same seeded state; compare
-    everything after every step.  Returns a small summary dict."""
+    everything after every step.  Each side carries its own theta and m from
+    step to step (independent trajectories: the device state is never reset
+    from the oracle's).  Returns a small summary dict."""
     import torch
     rs = np.random.default_rng(1234 + seed_shift)
     theta = gen.host_theta(wl)
@@ -94,8 +115,7 @@ def gpu_step_vs_oracle(wl, steps=2, t0=1, zeros=True, debug=True, seed_shift=0):
     for t in range(t0, t0 + steps):
         g = gen.host_g(wl, t)
         if zeros:
-            inject_zeros(wl, m, g, rs)
-            d_m.copy_(to_dev(m))
+            zero_device_m(d_m, wl, inject_zeros(wl, m, g, rs))
         d_g = to_dev(g, gb)
         dbg = None
         if debug:

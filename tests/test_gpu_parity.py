@@ -198,6 +198,69 @@ def test_quant_l1_handworked():
     _quant_case(x, [("a", 5)], 3)
 
 
+def _m1_order_rows(cases, W):
+    """The hand-worked summation-order cases as consecutive tensors; worker
+    i holds the case vectors scaled by (-2)^i (exact at every tree level)."""
+    wl = wls.Workload(name="m1order", tensors=[(c["name"], c["n"]) for c in cases], W=W,
+                      agg="l1", qbits=4)
+    x = np.zeros((W, wl.ld), np.float32)
+    for T, c in enumerate(cases):
+        a = wl.offsets[T]
+        for k, e in c["place"]:
+            for i in range(W):
+                x[i, a + k] = np.float32((-2.0) ** i * 2.0**e)
+    return wl, x
+
+
+def _m1_worked(c):
+    from fractions import Fraction
+    return float(Fraction(float.fromhex(c["S"])) / c["n"])
+
+
+@pytest.mark.parametrize("big", [False, True], ids=["tensors", "many-groups"])
+def test_m1_order_handworked_gpu(big):
+    """The library's mean |x| against sums worked by hand from the written
+    summation order (tests/golden/m1_order.json), not against the oracle:
+    quad pairing, rounds in order, wave halving, block nesting, the group
+    fold, the final lanes over 34 and 65 groups of 256 blocks, the divisor.
+    Through the standalone quantiser (m1 output) and through the fused
+    step's norm pass (beta1 = 1/2, g = 0: c = m/2 exactly, so M1 halves)."""
+    import torch
+    cases = golden("m1_order.json")["cases"]
+    if big:
+        groups = [[c] for c in cases if c["n"] > (1 << 20)]
+    else:
+        small_cases = [c for c in cases if c["n"] <= (1 << 20)]
+        groups = [sorted(small_cases, key=lambda c: c["n"] % 64 != 0)]
+    for cs in groups:
+        W = 1 if big else 2
+        wl, x = _m1_order_rows(cs, W)
+        want = np.array([[2.0**i * _m1_worked(c) for c in cs] for i in range(W)])
+        lc = lioncub_for(wl)
+        codes = torch.zeros((W, wl.ld), dtype=torch.int8, device="cuda")
+        m1 = torch.zeros((W, wl.n_tensors), dtype=torch.float64, device="cuda")
+        lc.quant_l1(to_dev(x), codes, m1)
+        torch.cuda.synchronize()
+        got = to_host(m1)
+        assert np.array_equal(got.view(np.uint64), want.view(np.uint64)), (got, want)
+        lc.close()
+        for gdt in ("f32", "bf16"):
+            wl2 = wl.with_(beta1=0.5, grad_dtype=gdt)
+            lc = lioncub_for(wl2)
+            theta = torch.zeros(wl.d, dtype=torch.float32, device="cuda")
+            d_m = to_dev(x)
+            g = torch.zeros((W, wl.ld), dtype=torch.bfloat16 if gdt == "bf16" else torch.float32,
+                            device="cuda")
+            m1s = torch.zeros((W, wl.n_tensors), dtype=torch.float64, device="cuda")
+            lc.step(theta, d_m, g, 1, {"m1": m1s})
+            torch.cuda.synchronize()
+            got = to_host(m1s)
+            assert np.array_equal(got.view(np.uint64), (want * 0.5).view(np.uint64)), (got, want)
+            lc.close()
+        del x
+        print("m1 order", [c["name"] for c in cs], "ok", flush=True)
+
+
 @pytest.mark.parametrize("qbits", [2, 4, 8])
 def test_quant_l1_adversarial_magnitudes(qbits):
     """Magnitudes over 1e-30..1e30 make the fp64 sum order-sensitive: the

@@ -358,6 +358,60 @@ def test_m1_within_summation_error_bound(oracle, n):
     assert abs(oracle.m1(y) * n - exact) > bound
 
 
+def _m1_case_row(case):
+    """The case's vector: zeros with 2^e at each placed local index."""
+    x = np.zeros(case["n"], np.float32)
+    for k, e in case["place"]:
+        x[k] = np.float32(2.0**e)
+    return x
+
+
+def _m1_expected(S_hex, n):
+    """S / n in one correctly rounded division (Fraction -> float rounds once)."""
+    return float(Fraction(float.fromhex(S_hex)) / n)
+
+
+@pytest.mark.parametrize("case", golden("m1_order.json")["cases"], ids=lambda c: c["name"])
+def test_m1_order_handworked(oracle, case):
+    """The fixed summation tree of M1 at each of its levels (quad pairing,
+    rounds in order, wave halving, block nesting, group fold, final lane runs
+    and halving, the element-count divisor), against sums worked by hand from
+    the written order; each case also states what a different order would
+    give, and that value must differ after the division, so a slip at that
+    level in the oracle fails here."""
+    x = _m1_case_row(case)
+    want = _m1_expected(case["S"], case["n"])
+    for alt in case["alternatives"].values():
+        assert _m1_expected(alt, case["n"]) != want
+    assert oracle.m1(x) == want
+    # the sign of a value does not enter, and an exact power-of-two scale
+    # passes through every level unchanged
+    assert oracle.m1(-x) == want
+    assert oracle.m1(x * np.float32(0.25)) == want * 0.25
+
+
+def test_m1_order_per_tensor_and_worker(oracle):
+    """The same hand-worked cases laid out as consecutive tensors of one
+    vector (local indices count from each tensor's first element) for two
+    workers, the second scaled by 2: the standalone quantiser's per-(worker,
+    tensor) M1 must equal every case's worked value."""
+    cases = [c for c in golden("m1_order.json")["cases"] if c["n"] <= (1 << 20)]
+    # the ragged case has a length that is not a multiple of 64: it goes last
+    cases.sort(key=lambda c: c["n"] % 64 != 0)
+    wl = wls.Workload(name="m1order", tensors=[(c["name"], c["n"]) for c in cases], W=2,
+                      agg="l1", qbits=4)
+    x = np.zeros((2, wl.ld), np.float32)
+    for T, c in enumerate(cases):
+        a = wl.offsets[T]
+        x[0, a:a + c["n"]] = _m1_case_row(c)
+        x[1, a:a + c["n"]] = -2 * _m1_case_row(c)
+    _, m1v = oracle.quant_l1(wl, x)
+    for T, c in enumerate(cases):
+        want = _m1_expected(c["S"], c["n"])
+        assert m1v[0, T] == want, c["name"]
+        assert m1v[1, T] == 2 * want, c["name"]
+
+
 def test_m1_block_reads_past_n_as_zero(oracle):
     rs = np.random.default_rng(2)
     for n in (1, 5, 1000, 4095):
@@ -735,6 +789,22 @@ def test_splitmix64_published_outputs(oracle):
     want = [int(v) for v in gd["seed_1234567_first5"]]
     assert [oracle.splitmix64(1234567, k) for k in range(5)] == want
     assert oracle.splitmix64(0, 0) == int(gd["seed_0_first"])
+
+
+def test_sr_draws_land_on_published_outputs(oracle):
+    """The draw mapping (which SplitMix64 output and which half an element
+    takes) against tuples worked by hand to land on the stream's published
+    first five outputs: the expected 32 bits are sliced from those published
+    values, not recomputed by the generator.  Exercises d, W, t, i, the
+    even/odd half and the counter's wrap-around mod 2^64."""
+    pub = [int(v) for v in golden("splitmix64.json")["seed_1234567_first5"]]
+    gd = golden("sr_draws.json")
+    assert gd["seed"] == 1234567
+    for tp in gd["tuples"]:
+        v = pub[tp["output"]]
+        want = v >> 32 if tp["half"] == "high" else v & 0xFFFFFFFF
+        got = oracle.sr_u32(gd["seed"], tp["d"], tp["W"], tp["t"], tp["i"], tp["j"])
+        assert got == want, tp
 
 
 def test_minf_is_numpy_max_abs(oracle):
