@@ -12,7 +12,9 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "liblioncub.so")
 
-OK, EINVAL, EALIGN, EWORKSPACE, EDEVICE, EUNSUPPORTED, ENOMEM = 0, -1, -2, -3, -4, -5, -6
+OK, EINVAL, EALIGN, EWORKSPACE, EDEVICE, EUNSUPPORTED, ENOMEM, ESCRATCH = (
+    0, -1, -2, -3, -4, -5, -6, -7)
+STATIC_SCRATCH_BYTES = 64 << 20   # LIONCUB_STATIC_SCRATCH_BYTES
 F32, BF16 = 0, 1
 AGG_VOTE, AGG_L1SUM, AGG_AVG, AGG_LINFSUM = 0, 1, 2, 3
 TIE_PARITY, TIE_ZERO = 0, 1
@@ -25,6 +27,7 @@ KERNEL_NAMES = ["vote_step", "m1_partial", "m1_finalize", "l1_step", "pack", "vo
                 "linf_step", "quant_linf", "unpack_bits"]
 
 EXPORTS = ["lioncub_workspace_bytes", "lioncub_init", "lioncub_set_stream", "lioncub_step",
+           "lioncub_step_static",
            "lioncub_pack", "lioncub_vote", "lioncub_quant_l1", "lioncub_quant_linf",
            "lioncub_vote_bits",
            "lioncub_apply", "lioncub_pack_codes", "lioncub_unpack_sum", "lioncub_unpack_sum_bits",
@@ -69,6 +72,8 @@ def lib():
         L.lioncub_set_stream.restype = C.c_int
         L.lioncub_step.argtypes = [vp, vp, vp, vp, i64, C.POINTER(lioncub_debug)]
         L.lioncub_step.restype = C.c_int
+        L.lioncub_step_static.argtypes = [cfgp, vp, vp, vp, vp, i64]
+        L.lioncub_step_static.restype = C.c_int
         L.lioncub_pack.argtypes = [vp, vp, i64, vp]
         L.lioncub_pack.restype = C.c_int
         L.lioncub_vote.argtypes = [vp, vp, i64, vp, vp]
@@ -169,6 +174,13 @@ def lioncub_step(ctx, theta, m, g, t, dbg=None):
                                       "stats", "mvar_max")))
     _check("lioncub_step", lib().lioncub_step(ctx, _ptr(theta), _ptr(m), _ptr(g), int(t),
                                               C.byref(d) if d is not None else None))
+
+
+def lioncub_step_static(cfg, stream, theta, m, g, t):
+    """The allocation-free step: no context, no workspace (the library's
+    fixed scratch array); `stream` is a HIP stream handle (c_void_p)."""
+    _check("lioncub_step_static", lib().lioncub_step_static(C.byref(cfg), stream, _ptr(theta),
+                                                            _ptr(m), _ptr(g), int(t)))
 
 
 def lioncub_pack(ctx, x, t, bits):

@@ -10,7 +10,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "liblioncub.so")
-SOURCES = ["lioncub.cpp", "step.hip", "l1.hip", "bits.hip", "wire.hip", "stream.hip"]
+SOURCES = ["lioncub.cpp", "tables.hip", "static.hip", "step.hip", "l1.hip", "bits.hip",
+           "wire.hip", "stream.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

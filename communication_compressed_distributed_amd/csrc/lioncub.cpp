@@ -1,7 +1,8 @@
 // lioncub.cpp -- C ABI of the Lion Cub compressed-update step (see
-// include/lioncub.h): configuration checks, workspace layout, tensor and
-// block tables, kernel selection, profiling hook.  No device memory is
-// allocated here; the caller provides the workspace.
+// include/lioncub.h): configuration checks, workspace layout, kernel
+// selection, profiling hook.  No device memory is allocated here; the caller
+// provides the workspace (the allocation-free step in static.hip uses a
+// fixed device array instead).
 #include "lioncub.h"
 
 #include <hip/hip_runtime.h>
@@ -11,6 +12,7 @@
 #include <new>
 #include <vector>
 
+#include "ctx.hpp"
 #include "layout.hpp"
 
 namespace lioncub {
@@ -41,16 +43,15 @@ hipError_t launch_stream(int kind, const float* a, const float* b, float* c, int
 
 using namespace lioncub;
 
-namespace {
+namespace lioncub {
 
-constexpr size_t kWsAlign = 256;
+namespace {
 constexpr int64_t kMaxLd = int64_t{1} << 40;
 
-struct WsLayout {
-  size_t blk, tens, grp, partial, gval, m1, scale, bstat, gstat, total;
-};
-
 size_t align_up(size_t x) { return (x + kWsAlign - 1) / kWsAlign * kWsAlign; }
+
+bool finite(float x) { return std::isfinite(x); }
+}  // namespace
 
 WsLayout ws_layout(int64_t nblk, int64_t ngrp, int64_t nT, int64_t W) {
   WsLayout L;
@@ -76,8 +77,6 @@ WsLayout ws_layout(int64_t nblk, int64_t ngrp, int64_t nT, int64_t W) {
   L.total = o;
   return L;
 }
-
-bool finite(float x) { return std::isfinite(x); }
 
 // Checks every field; on success *nblk = number of tensor-aligned blocks and
 // *ngrp = number of groups of kGroup consecutive blocks (per tensor).
@@ -116,37 +115,23 @@ int check_config(const lioncub_config* c, int64_t* nblk, int64_t* ngrp) {
   return LIONCUB_OK;
 }
 
-bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+void bind_workspace(lioncub_ctx* c, char* ws, const WsLayout& L) {
+  c->blk = reinterpret_cast<BlockEnt*>(ws + L.blk);
+  c->tens = reinterpret_cast<TensorEnt*>(ws + L.tens);
+  c->grp = reinterpret_cast<GroupEnt*>(ws + L.grp);
+  c->partial = reinterpret_cast<double*>(ws + L.partial);
+  c->gval = reinterpret_cast<double*>(ws + L.gval);
+  c->m1 = reinterpret_cast<double*>(ws + L.m1);
+  c->scale = reinterpret_cast<double*>(ws + L.scale);
+  c->bstat = reinterpret_cast<uint64_t*>(ws + L.bstat);
+  c->gstat = reinterpret_cast<uint64_t*>(ws + L.gstat);
+}
 
-}  // namespace
-
-struct lioncub_ctx {
-  lioncub_config cfg;  // host pointers cleared after init
-  hipStream_t stream;
-  int32_t nblk;
-  int32_t ngrp;
-  int32_t any_sync;
-  BlockEnt* blk;
-  TensorEnt* tens;
-  GroupEnt* grp;
-  double* partial;
-  double* gval;
-  double* m1;
-  double* scale;
-  uint64_t* bstat;
-  uint64_t* gstat;
-  std::vector<BlockEnt> h_blk;
-  std::vector<TensorEnt> h_tens;
-  std::vector<GroupEnt> h_grp;
-  // profiling hook
-  bool prof = false;
-  int32_t prof_cap = 0;
-  int32_t prof_n = 0;
-  std::vector<hipEvent_t> prof_ev;  // 2 per record
-  std::vector<int32_t> prof_kind;
-};
+}  // namespace lioncub
 
 namespace {
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 // Launch through the profiling hook when it is on.
 template <typename F>
@@ -239,65 +224,11 @@ int lioncub_init(lioncub_ctx** out, const lioncub_config* cfg, void* hip_stream,
   c->stream = static_cast<hipStream_t>(hip_stream);
   c->nblk = static_cast<int32_t>(nblk);
   c->ngrp = static_cast<int32_t>(ngrp);
-  char* ws = static_cast<char*>(workspace);
-  c->blk = reinterpret_cast<BlockEnt*>(ws + L.blk);
-  c->tens = reinterpret_cast<TensorEnt*>(ws + L.tens);
-  c->grp = reinterpret_cast<GroupEnt*>(ws + L.grp);
-  c->partial = reinterpret_cast<double*>(ws + L.partial);
-  c->gval = reinterpret_cast<double*>(ws + L.gval);
-  c->m1 = reinterpret_cast<double*>(ws + L.m1);
-  c->scale = reinterpret_cast<double*>(ws + L.scale);
-  c->bstat = reinterpret_cast<uint64_t*>(ws + L.bstat);
-  c->gstat = reinterpret_cast<uint64_t*>(ws + L.gstat);
-
-  // the host tables are sized once, so nothing below can throw
-  try {
-    c->h_tens.resize(cfg->n_tensors);
-    c->h_blk.reserve(nblk);
-    c->h_grp.reserve(ngrp);
-  } catch (const std::bad_alloc&) {
-    delete c;
-    return LIONCUB_ENOMEM;
-  }
-  for (int T = 0; T < cfg->n_tensors; ++T) {
-    const int64_t a = cfg->tensor_offsets[T], n = cfg->tensor_offsets[T + 1] - a;
-    TensorEnt& te = c->h_tens[T];
-    te.off = a;
-    te.n = n;
-    te.blk0 = static_cast<int32_t>(c->h_blk.size());
-    te.nblk = static_cast<int32_t>((n + kBlock - 1) / kBlock);
-    te.grp0 = static_cast<int32_t>(c->h_grp.size());
-    te.ngrp = (te.nblk + kGroup - 1) / kGroup;
-    te.sync = cfg->sync_m ? (cfg->sync_m[T] ? 1 : 0) : 0;
-    c->any_sync |= te.sync;
-    te.pad = 0;
-    for (int32_t gq = 0; gq < te.ngrp; ++gq) {
-      GroupEnt ge;
-      ge.tensor = T;
-      ge.blk = te.blk0 + gq * kGroup;
-      ge.cnt = te.nblk - gq * kGroup < kGroup ? te.nblk - gq * kGroup : kGroup;
-      ge.pad = 0;
-      c->h_grp.push_back(ge);
-    }
-    for (int64_t s = 0; s < n; s += kBlock) {
-      BlockEnt be;
-      be.start = a + s;
-      be.len = static_cast<int32_t>(n - s < kBlock ? n - s : kBlock);
-      be.tensor = T;
-      c->h_blk.push_back(be);
-    }
-  }
+  bind_workspace(c, static_cast<char*>(workspace), L);
+  hipError_t e =
+      build_tables(cfg, nblk, ngrp, c->tens, c->blk, c->grp, &c->any_sync, c->stream);
   c->cfg.tensor_offsets = nullptr;
   c->cfg.sync_m = nullptr;
-
-  hipError_t e = hipMemcpyAsync(c->blk, c->h_blk.data(), c->h_blk.size() * sizeof(BlockEnt),
-                                hipMemcpyHostToDevice, c->stream);
-  if (e == hipSuccess)
-    e = hipMemcpyAsync(c->tens, c->h_tens.data(), c->h_tens.size() * sizeof(TensorEnt),
-                       hipMemcpyHostToDevice, c->stream);
-  if (e == hipSuccess)
-    e = hipMemcpyAsync(c->grp, c->h_grp.data(), c->h_grp.size() * sizeof(GroupEnt),
-                       hipMemcpyHostToDevice, c->stream);
   if (e == hipSuccess) e = hipStreamSynchronize(c->stream);
   if (e != hipSuccess) {
     delete c;
@@ -567,6 +498,8 @@ const char* lioncub_strerror(int status) {
     case LIONCUB_EDEVICE: return "HIP runtime or kernel launch failure";
     case LIONCUB_EUNSUPPORTED: return "configuration not supported by this build";
     case LIONCUB_ENOMEM: return "out of host memory";
+    case LIONCUB_ESCRATCH:
+      return "configuration needs more than the library's fixed scratch array";
     default: return "unknown status";
   }
 }

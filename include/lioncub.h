@@ -63,8 +63,11 @@ enum {
   LIONCUB_EWORKSPACE = -3,   /* workspace missing, misaligned or too small */
   LIONCUB_EDEVICE = -4,      /* HIP runtime / launch failure              */
   LIONCUB_EUNSUPPORTED = -5, /* valid request this build does not support */
-  LIONCUB_ENOMEM = -6        /* host memory for the context's tables or
+  LIONCUB_ENOMEM = -6,       /* host memory for the context or its
                                 profiling events could not be allocated   */
+  LIONCUB_ESCRATCH = -7      /* lioncub_step_static: the configuration
+                                needs more than the library's fixed device
+                                scratch array (LIONCUB_STATIC_SCRATCH_BYTES) */
 };
 
 enum { LIONCUB_F32 = 0, LIONCUB_BF16 = 1 };
@@ -80,10 +83,11 @@ typedef struct {
   int32_t n_tensors;             /* tensors in the flat vector, >= 1             */
   const int64_t *tensor_offsets; /* HOST, n_tensors+1: off[0]=0 < off[1] < ... <
                                     off[n]=d; off[k] % 64 == 0 for k < n.  Read
-                                    during lioncub_init only.                    */
+                                    during lioncub_init (or lioncub_step_static) only. */
   const uint8_t *sync_m;         /* HOST, n_tensors flags (1 = momentum averaged
                                     over workers on averaging steps) or NULL.
-                                    Read during lioncub_init only.               */
+                                    Read during lioncub_init (or
+                                    lioncub_step_static) only.                   */
   int32_t sync_every;            /* >= 1: averaging on steps with t % sync_every == 0 */
   int32_t theta_dtype;           /* LIONCUB_F32 or LIONCUB_BF16                  */
   int32_t grad_dtype;            /* LIONCUB_F32 or LIONCUB_BF16; m is always fp32 */
@@ -136,10 +140,11 @@ size_t lioncub_workspace_bytes(const lioncub_config *cfg);
 
 /* Validate cfg, lay out the caller's workspace (device, >= the bytes above,
  * 256-byte aligned, owned by the caller, must outlive the context and not be
- * touched by the caller while the context lives) and upload the tensor and
- * block tables into it on hip_stream (a hipStream_t; NULL = the null stream).
- * Synchronises that stream once.  On success *out receives a new context;
- * LIONCUB_ENOMEM if its host-side tables cannot be allocated. */
+ * touched by the caller while the context lives) and write the tensor, block
+ * and group tables into it on hip_stream (a hipStream_t; NULL = the null
+ * stream) with kernel launches.  Synchronises that stream once.  On success
+ * *out receives a new context; LIONCUB_ENOMEM if the context's host memory
+ * cannot be allocated. */
 int lioncub_init(lioncub_ctx **out, const lioncub_config *cfg, void *hip_stream,
                  void *workspace, size_t ws_bytes);
 
@@ -160,6 +165,32 @@ int lioncub_set_stream(lioncub_ctx *ctx, void *hip_stream);
  * fused quantise-sum-apply). */
 int lioncub_step(lioncub_ctx *ctx, void *theta, float *m, const void *g, int64_t t,
                  const lioncub_debug *dbg);
+
+/* For callers that cannot allocate any memory -- code under stream capture,
+ * tight serving loops, harnesses that forbid allocation: lioncub_step
+ * without a context or a caller workspace.  The tables and norm partials of
+ * the step live in a fixed array of device memory inside the library,
+ * LIONCUB_STATIC_SCRATCH_BYTES per GPU, which each GPU the library runs on
+ * holds from the time the library's code is loaded there until the process
+ * ends.  The call allocates nothing (host or device), enqueues kernel
+ * launches only on hip_stream (a hipStream_t of the current device, NULL =
+ * its null stream) and rebuilds the tables in the array every call, so it
+ * carries no state from one call to the next and needs no set-up or
+ * teardown.
+ *   cfg:   as for lioncub_init (its host arrays are read during the call
+ *          only); the configuration must satisfy lioncub_workspace_bytes(cfg)
+ *          <= LIONCUB_STATIC_SCRATCH_BYTES, else LIONCUB_ESCRATCH and
+ *          nothing is enqueued
+ *   theta, m, g, t: as for lioncub_step (no debug outputs)
+ * Every call on one GPU shares that GPU's array: calls that overlap on one
+ * GPU (on two streams, or from two host threads) race and their results are
+ * undefined; calls ordered on one stream are safe.  LIONCUB_EINVAL if
+ * hip_stream belongs to another device than the current one.  The first call
+ * on each device looks up the array's device address there (the only
+ * call that may synchronise). */
+#define LIONCUB_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+int lioncub_step_static(const lioncub_config *cfg, void *hip_stream, void *theta, float *m,
+                        const void *g, int64_t t);
 
 /* Sign packing of x = c directly: bits[W][ld/64] (device) from x[W][ld]
  * (device fp32), zeros by the parity of t (>= 1).  Every word of every row is

@@ -28,9 +28,28 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_strerror_names_every_status():
-    for s in (0, -1, -2, -3, -4, -5, -6):
+    for s in (0, -1, -2, -3, -4, -5, -6, -7):
         assert _abi.lioncub_strerror(s) != "unknown status"
     assert _abi.lioncub_strerror(7) == "unknown status"
+
+
+def test_step_static_rejects_before_device():
+    """The allocation-free step checks its configuration, its pointers and
+    the size of the fixed scratch array before any HIP call."""
+    L = _abi.lib()
+    p = C.c_void_p(4096)
+    for bad in (dict(W=0), dict(ld=10000), dict(tensor_offsets=[0, 4000, 10000])):
+        assert L.lioncub_step_static(C.byref(cfg(**bad)), None, p, p, p, 1) == _abi.EINVAL
+    c = cfg()
+    assert L.lioncub_step_static(None, None, p, p, p, 1) == _abi.EINVAL
+    assert L.lioncub_step_static(C.byref(c), None, None, p, p, 1) == _abi.EINVAL
+    assert L.lioncub_step_static(C.byref(c), None, p, p, p, 0) == _abi.EINVAL
+    assert L.lioncub_step_static(C.byref(c), None, C.c_void_p(4100), p, p, 1) == _abi.EALIGN
+    # the need is exactly lioncub_workspace_bytes: fits up to the array size
+    big = cfg(d=350_000_000, ld=350_000_000, W=128, tensor_offsets=[0, 350_000_000])
+    assert _abi.lioncub_workspace_bytes(big) > _abi.STATIC_SCRATCH_BYTES
+    assert L.lioncub_step_static(C.byref(big), None, p, p, p, 1) == _abi.ESCRATCH
+    assert "scratch" in _abi.lioncub_strerror(_abi.ESCRATCH)
 
 
 def cfg(**kw):
