@@ -113,6 +113,35 @@ def run_fullsize(wl, steps, tensors=None, n_random=6):
     torch.cuda.empty_cache()
 
 
+def run_every_element(wl, steps):
+    """The workload at its real size for its steps, every element of theta
+    and m (and every norm) compared with the oracle after every step; each
+    side carries its own state, the device's is never reset."""
+    import torch
+    from tests.fullsize_check import check_step_every_element
+    torch.cuda.set_device(0)
+    _say(wl.name, f"every element: d={wl.d} W={wl.W} steps={steps}")
+    theta = gen.device_theta(wl)
+    m = gen.device_m(wl)
+    g = gen.device_g(wl, steps[0])
+    lc = lioncub_for(wl)
+    for t in steps:
+        gen.fill_device_g(wl, t, g)
+        torch.cuda.synchronize()
+        check_step_every_element(wl, lc, theta, m, g, t)
+    lc.close()
+    del theta, m, g
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("wl", wls.ALL, ids=lambda w: w.name)
+def test_every_element_at_full_size(wl):
+    """All five workloads at their full shapes and step counts (10, 5, 5, 3
+    and 3 steps): every parameter, every momentum of every worker, and on
+    the L1 workloads the mean |c| of every (worker, tensor) pair."""
+    run_every_element(wl, list(range(1, wl.steps + 1)))
+
+
 def test_flat_1M_w4_vote_fullsize():
     run_fullsize(wls.FLAT_1M_W4_VOTE, steps=list(range(1, 11)))
 
