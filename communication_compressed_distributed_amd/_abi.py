@@ -18,7 +18,6 @@ STATIC_SCRATCH_BYTES = 64 << 20   # LIONCUB_STATIC_SCRATCH_BYTES
 F32, BF16 = 0, 1
 AGG_VOTE, AGG_L1SUM, AGG_AVG, AGG_LINFSUM = 0, 1, 2, 3
 TIE_PARITY, TIE_ZERO = 0, 1
-STREAM_READ, STREAM_COPY, STREAM_TRIAD = 0, 1, 2
 (K_VOTE_STEP, K_M1_PARTIAL, K_M1_FINALIZE, K_L1_STEP, K_PACK, K_VOTE, K_QUANT, K_VOTE_BITS,
  K_APPLY, K_PACK_CODES, K_UNPACK_SUM, K_AVG_STEP, K_STATS, K_LINF_STEP, K_QUANT_LINF,
  K_UNPACK_BITS, K_COUNT) = range(17)
@@ -32,7 +31,7 @@ EXPORTS = ["lioncub_workspace_bytes", "lioncub_init", "lioncub_set_stream", "lio
            "lioncub_vote_bits",
            "lioncub_apply", "lioncub_pack_codes", "lioncub_unpack_sum", "lioncub_unpack_sum_bits",
            "lioncub_profile_begin",
-           "lioncub_profile_end", "lioncub_stream_probe", "lioncub_destroy", "lioncub_strerror"]
+           "lioncub_profile_end", "lioncub_destroy", "lioncub_strerror"]
 
 
 class lioncub_config(C.Structure):
@@ -96,8 +95,6 @@ def lib():
         L.lioncub_profile_begin.restype = C.c_int
         L.lioncub_profile_end.argtypes = [vp, C.POINTER(C.c_double), C.POINTER(C.c_int32)]
         L.lioncub_profile_end.restype = C.c_int
-        L.lioncub_stream_probe.argtypes = [i32, vp, vp, vp, i64, vp]
-        L.lioncub_stream_probe.restype = C.c_int
         L.lioncub_destroy.argtypes = [vp]
         L.lioncub_destroy.restype = C.c_int
         L.lioncub_strerror.argtypes = [C.c_int]
@@ -233,11 +230,6 @@ def lioncub_profile_end(ctx):
     n = (C.c_int32 * K_COUNT)()
     _check("lioncub_profile_end", lib().lioncub_profile_end(ctx, ms, n))
     return {KERNEL_NAMES[k]: (ms[k], n[k]) for k in range(K_COUNT)}
-
-
-def lioncub_stream_probe(kind, a, b, c, n, stream):
-    _check("lioncub_stream_probe",
-           lib().lioncub_stream_probe(int(kind), _ptr(a), _ptr(b), _ptr(c), int(n), stream))
 
 
 def lioncub_destroy(ctx):

@@ -11,7 +11,11 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "liblioncub.so")
 SOURCES = ["lioncub.cpp", "tables.hip", "static.hip", "step.hip", "l1.hip", "bits.hip",
-           "wire.hip", "stream.hip"]
+           "wire.hip"]
+# The measurement library (include/lioncub_probe.h): reference streams and the
+# step-pattern probe, kept out of liblioncub.so.
+PROBE_LIB = os.path.join(HERE, "liblioncub_probe.so")
+PROBE_SOURCES = ["probe/probe.cpp", "probe/stream.hip", "probe/pattern.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
@@ -24,11 +28,12 @@ OBJ = os.path.join(ROOT, "_build")
 
 
 def build(verbose=False, jobs=None):
-    """Compile every source to an object in parallel (the step kernels'
-    template instantiations dominate), then link the shared library."""
+    """Compile every source of both libraries to objects in parallel (the
+    step kernels' template instantiations dominate), then link
+    liblioncub.so and the measurement library liblioncub_probe.so."""
     from concurrent.futures import ThreadPoolExecutor
 
-    os.makedirs(OBJ, exist_ok=True)
+    os.makedirs(os.path.join(OBJ, "probe"), exist_ok=True)
     inc = ["-I", os.path.join(ROOT, "include"), "-I", CSRC]
 
     def compile_one(src):
@@ -39,15 +44,20 @@ def build(verbose=False, jobs=None):
         subprocess.run(cmd, check=True)
         return obj
 
-    jobs = jobs or min(len(SOURCES), os.cpu_count() or 1)
+    def link(lib, objs):
+        tmp = lib + ".tmp"
+        cmd = [HIPCC, "--offload-arch=gfx950", "-fPIC", "-shared", "-o", tmp, *objs]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, lib)
+
+    srcs = SOURCES + PROBE_SOURCES
+    jobs = jobs or min(len(srcs), os.cpu_count() or 1)
     with ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(compile_one, SOURCES))
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, "--offload-arch=gfx950", "-fPIC", "-shared", "-o", tmp, *objs]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
+        objs = list(ex.map(compile_one, srcs))
+    link(LIB, objs[: len(SOURCES)])
+    link(PROBE_LIB, objs[len(SOURCES):])
     return LIB
 
 

@@ -37,8 +37,6 @@ hipError_t launch_unpack_sum(const uint32_t* wire, int32_t* sums, int8_t* sign, 
                              int64_t ld, int W, int n, hipStream_t st);
 hipError_t launch_unpack_bits(const uint32_t* wire, uint64_t* sign_bits, uint64_t* zero_bits,
                               int64_t d, int64_t ld, int W, int n, hipStream_t st);
-hipError_t launch_stream(int kind, const float* a, const float* b, float* c, int64_t n,
-                         hipStream_t st);
 }  // namespace lioncub
 
 using namespace lioncub;
@@ -421,15 +419,6 @@ int lioncub_quant_linf(lioncub_ctx* ctx, const float* x, int64_t t, int8_t* code
     e = run(ctx, LIONCUB_K_QUANT_LINF,
             [&] { return launch_quant_codes(q, codes, 1, ctx->stream); });
   return dev_status(e);
-}
-
-int lioncub_stream_probe(int32_t kind, const float* a, const float* b, float* c, int64_t n,
-                         void* hip_stream) {
-  if (kind < LIONCUB_STREAM_READ || kind > LIONCUB_STREAM_TRIAD) return LIONCUB_EINVAL;
-  if (n < kBlock || n % kBlock != 0 || n / kBlock > 0x7FFFFFFF) return LIONCUB_EINVAL;
-  if (!a || !c || (kind == LIONCUB_STREAM_TRIAD && !b)) return LIONCUB_EINVAL;
-  if (!aligned(a, 16) || !aligned(b, 16) || !aligned(c, 16)) return LIONCUB_EALIGN;
-  return dev_status(launch_stream(kind, a, b, c, n, static_cast<hipStream_t>(hip_stream)));
 }
 
 int lioncub_profile_begin(lioncub_ctx* ctx, int32_t capacity) {

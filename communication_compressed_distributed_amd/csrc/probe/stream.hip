@@ -1,10 +1,10 @@
-// stream.hip -- STREAM-style reference kernels for the measurement hook
-// lioncub_stream_probe: what plain read-only, copy and triad streams achieve
-// on this device, reported beside the published 8 TB/s peak.  Same shape as
-// the library's kernels: 256 threads, 4096 elements per workgroup, four
-// nontemporal 16-byte quads per lane.
-#include "device.hpp"
-#include "layout.hpp"
+// stream.hip -- STREAM-style reference kernels of the measurement library
+// (lioncub_probe_stream): what plain read-only, copy and triad streams
+// achieve on this device, reported beside the published 8 TB/s peak.  Same
+// shape as the step library's kernels: 256 threads, 4096 elements per
+// workgroup, four nontemporal 16-byte quads per lane.
+#include "../device.hpp"
+#include "../layout.hpp"
 
 namespace lioncub {
 

@@ -312,20 +312,6 @@ enum {
 int lioncub_profile_begin(lioncub_ctx *ctx, int32_t capacity);
 int lioncub_profile_end(lioncub_ctx *ctx, double *ms_total, int32_t *launches);
 
-/* Measurement hook, outside the method: a STREAM-style reference kernel
- * with the library's own launch shape (256 threads, 4096 elements per
- * workgroup, nontemporal 16-byte accesses), so a benchmark can report what
- * plain streams reach on the device beside the published peak.
- *   LIONCUB_STREAM_READ:  reads a[n] (c receives nothing; pass any buffer)
- *   LIONCUB_STREAM_COPY:  c[j] = a[j]
- *   LIONCUB_STREAM_TRIAD: c[j] = a[j] + 0.5f * b[j]
- * a, b, c: device fp32, 16-byte aligned, not overlapping (b only for the
- * triad); n: elements, a positive multiple of 4096.  Asynchronous on
- * hip_stream (a hipStream_t, NULL = the null stream); needs no context. */
-enum { LIONCUB_STREAM_READ = 0, LIONCUB_STREAM_COPY = 1, LIONCUB_STREAM_TRIAD = 2 };
-int lioncub_stream_probe(int32_t kind, const float *a, const float *b, float *c, int64_t n,
-                         void *hip_stream);
-
 /* Release the context (host memory).  Synchronises its stream first.  NULL
  * is accepted. */
 int lioncub_destroy(lioncub_ctx *ctx);

@@ -145,16 +145,6 @@ def test_null_context_and_arguments_rejected():
     assert L.lioncub_destroy(None) == _abi.OK
 
 
-def test_stream_probe_rejects_bad_arguments_before_device():
-    L = _abi.lib()
-    p = C.c_void_p(256)
-    assert L.lioncub_stream_probe(3, p, p, p, 4096, None) == _abi.EINVAL        # kind
-    assert L.lioncub_stream_probe(0, p, p, p, 4095, None) == _abi.EINVAL        # n % 4096
-    assert L.lioncub_stream_probe(0, p, p, p, 0, None) == _abi.EINVAL
-    assert L.lioncub_stream_probe(2, p, None, p, 4096, None) == _abi.EINVAL     # triad needs b
-    assert L.lioncub_stream_probe(1, C.c_void_p(260), p, p, 4096, None) == _abi.EALIGN
-
-
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     """No fallback: without the built library the product path raises."""
     monkeypatch.setattr(_abi, "_lib", None)

@@ -25,8 +25,18 @@ def test_threaded_oracle_step_equals_whole_step(oracle, agg, qbits, gdt, P):
     assert np.array_equal(m1, m2)
 
 
-def test_cpu_threads_is_bounded():
-    assert 1 <= bench.cpu_threads() <= 16
+def test_cpu_threads_uses_every_allowed_cpu_within_the_quota(monkeypatch):
+    import os
+    P, host = bench.cpu_threads()
+    assert host["host_cpus"] == os.cpu_count()
+    assert host["allowed_cpus"] == len(os.sched_getaffinity(0))
+    assert 1 <= P <= host["allowed_cpus"]
+    if host["cgroup_cpu_quota"] is None:
+        assert P == host["allowed_cpus"]
+    monkeypatch.setattr(bench, "cpu_quota", lambda: 2.5)
+    assert bench.cpu_threads()[0] == min(2, host["allowed_cpus"])
+    monkeypatch.setattr(bench, "cpu_quota", lambda: None)
+    assert bench.cpu_threads()[0] == host["allowed_cpus"]
 
 
 def test_gpus_above_one_exit_with_a_message(capsys):

@@ -110,30 +110,6 @@ def test_step_captured_in_a_graph_and_replayed(agg):
     le.close()
 
 
-def test_stream_probe_kernels():
-    """The measurement hook's reference kernels compute what they claim:
-    copy c = a, triad c = a + 0.5 b (0.5 b is exact, so one rounding)."""
-    import torch
-
-    from communication_compressed_distributed_amd import _abi
-    n = 3 * 4096
-    rs = np.random.default_rng(2)
-    a_h = rs.normal(0, 1, n).astype(np.float32)
-    b_h = rs.normal(0, 1, n).astype(np.float32)
-    a, b = to_dev(a_h), to_dev(b_h)
-    c = torch.full((n,), 7.0, device="cuda")
-    h = _abi._stream_handle()
-    _abi.lioncub_stream_probe(_abi.STREAM_READ, a, None, c, n, h)
-    torch.cuda.synchronize()
-    assert torch.all(c == 7.0)                 # the read kernel writes nothing
-    _abi.lioncub_stream_probe(_abi.STREAM_COPY, a, None, c, n, h)
-    torch.cuda.synchronize()
-    assert np.array_equal(to_host(c), a_h)
-    _abi.lioncub_stream_probe(_abi.STREAM_TRIAD, a, b, c, n, h)
-    torch.cuda.synchronize()
-    assert np.array_equal(to_host(c), a_h + np.float32(0.5) * b_h)
-
-
 def test_two_contexts_from_two_host_threads():
     """The library keeps no global state: two host threads, each with its own
     context and stream, step concurrently (ctypes releases the GIL during
@@ -228,3 +204,59 @@ def test_capture_refuses_windows_that_would_not_replay_exactly():
     with pytest.raises(ValueError):
         li.capture(th, m, gs[:2], 1)                # max-norm draws depend on the full t
     li.close()
+
+
+def test_probe_stream_kernels():
+    """The measurement library's reference kernels compute what they claim:
+    copy c = a, triad c = a + 0.5 b (0.5 b is exact, so one rounding)."""
+    import torch
+
+    from communication_compressed_distributed_amd import _abi, _probe
+    n = 3 * 4096
+    rs = np.random.default_rng(2)
+    a_h = rs.normal(0, 1, n).astype(np.float32)
+    b_h = rs.normal(0, 1, n).astype(np.float32)
+    a, b = to_dev(a_h), to_dev(b_h)
+    c = torch.full((n,), 7.0, device="cuda")
+    h = _abi._stream_handle()
+    _probe.lioncub_probe_stream(_probe.PROBE_READ, a, None, c, n, h)
+    torch.cuda.synchronize()
+    assert torch.all(c == 7.0)                 # the read kernel writes nothing
+    _probe.lioncub_probe_stream(_probe.PROBE_COPY, a, None, c, n, h)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(c), a_h)
+    _probe.lioncub_probe_stream(_probe.PROBE_TRIAD, a, b, c, n, h)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(c), a_h + np.float32(0.5) * b_h)
+
+
+def test_probe_step_pattern_touches_every_element():
+    """The step-pattern probe reads and writes exactly the step's elements:
+    every worker's m becomes beta2*m + (1-beta2)*g (one rounding each, no
+    contraction), columns past d stay, and every theta moves by +-lr."""
+    import torch
+
+    from communication_compressed_distributed_amd import _abi, _probe
+    rs = np.random.default_rng(3)
+    for W, d, gd in ((16, 5 * 4096 + 900, 0), (5, 4096 + 64, 1), (8, 3 * 4096, 1)):
+        ld = (d + 63) // 64 * 64 + 64
+        th_h = rs.normal(0, 0.02, d).astype(np.float32)
+        m_h = rs.normal(0, 1e-3, (W, ld)).astype(np.float32)
+        g32 = rs.normal(0, 1e-3, (W, ld)).astype(np.float32)
+        th, m = to_dev(th_h), to_dev(m_h)
+        if gd:
+            g = torch.from_numpy(g32).to(torch.bfloat16).cuda()
+            gw = g.float().cpu().numpy()
+        else:
+            g = to_dev(g32)
+            gw = g32
+        beta2, lr = np.float32(0.99), np.float32(1e-4)
+        _probe.lioncub_probe_step_pattern(th, m, g, d, ld, W, 0, gd, float(beta2), float(lr),
+                                          _abi._stream_handle())
+        torch.cuda.synchronize()
+        want = (beta2 * m_h[:, :d]) + ((np.float32(1) - beta2) * gw[:, :d])
+        got = to_host(m)
+        assert np.array_equal(got[:, :d], want)
+        assert np.array_equal(got[:, d:], m_h[:, d:])
+        moved = to_host(th) - th_h
+        assert np.all((moved != 0))

@@ -20,7 +20,9 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 PKG = os.path.join(ROOT, "communication_compressed_distributed_amd")
 OBJ = os.path.join(ROOT, "_build")
-KERNEL_OBJS = ["step.hip.o", "l1.hip.o", "bits.hip.o", "wire.hip.o", "stream.hip.o"]
+KERNEL_OBJS = ["step.hip.o", "l1.hip.o", "bits.hip.o", "wire.hip.o"]
+# sources with host code of the C ABI, rebuilt here with host sanitizers
+HOST_SRCS = ["lioncub.cpp", "tables.hip", "static.hip"]
 
 
 def _run_child(code, preload, env_extra=None):
@@ -84,18 +86,21 @@ def test_host_library_under_asan_and_ubsan(tmp_path):
         pytest.skip("kernel objects not built (run __graft_entry__.build() first)")
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
     from communication_compressed_distributed_amd import build as libbuild
-    host_obj = str(tmp_path / "lioncub_san.o")
     lib = str(tmp_path / "liblioncub_san.so")
-    # sanitizer options on the host side only
-    subprocess.run([hipcc, *libbuild.FLAGS, "-Xarch_host", "-fsanitize=address",
-                    "-Xarch_host", "-fsanitize=undefined",
-                    "-Xarch_host", "-fno-sanitize-recover=undefined",
-                    "-Xarch_host", "-fno-omit-frame-pointer", "-g",
-                    "-I", os.path.join(ROOT, "include"), "-I", os.path.join(PKG, "csrc"),
-                    "-c", "-o", host_obj, os.path.join(PKG, "csrc", "lioncub.cpp")], check=True)
+    host_objs = []
+    for src in HOST_SRCS:
+        host_obj = str(tmp_path / (src + ".san.o"))
+        # sanitizer options on the host side only
+        subprocess.run([hipcc, *libbuild.FLAGS, "-Xarch_host", "-fsanitize=address",
+                        "-Xarch_host", "-fsanitize=undefined",
+                        "-Xarch_host", "-fno-sanitize-recover=undefined",
+                        "-Xarch_host", "-fno-omit-frame-pointer", "-g",
+                        "-I", os.path.join(ROOT, "include"), "-I", os.path.join(PKG, "csrc"),
+                        "-c", "-o", host_obj, os.path.join(PKG, "csrc", src)], check=True)
+        host_objs.append(host_obj)
     subprocess.run([hipcc, "--offload-arch=gfx950", "-fPIC", "-shared",
                     "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
-                    "-o", lib, host_obj, *objs], check=True)
+                    "-o", lib, *host_objs, *objs], check=True)
     rt = subprocess.run([hipcc.replace("bin/hipcc", "llvm/bin/clang"),
                          "-print-file-name=libclang_rt.asan-x86_64.so"],
                         capture_output=True, text=True, check=True).stdout.strip()
