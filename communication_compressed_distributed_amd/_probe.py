@@ -15,7 +15,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "liblioncub_probe.so")
 
 PROBE_READ, PROBE_COPY, PROBE_TRIAD = 0, 1, 2
-EXPORTS = ["lioncub_probe_stream", "lioncub_probe_step_pattern"]
+EXPORTS = ["lioncub_probe_stream", "lioncub_probe_step_pattern", "lioncub_probe_panel_pattern"]
 
 _lib = None
 
@@ -32,6 +32,9 @@ def lib():
         L.lioncub_probe_step_pattern.argtypes = [vp, vp, vp, i64, i64, i32, i32, i32, C.c_float,
                                                  C.c_float, vp]
         L.lioncub_probe_step_pattern.restype = C.c_int
+        L.lioncub_probe_panel_pattern.argtypes = [vp, vp, vp, i64, i64, i32, i32, i32, C.c_float,
+                                                  C.c_float, i32, vp]
+        L.lioncub_probe_panel_pattern.restype = C.c_int
         _lib = L
     return _lib
 
@@ -51,3 +54,11 @@ def lioncub_probe_step_pattern(theta, m, g, d, ld, W, theta_dtype, grad_dtype, b
            lib().lioncub_probe_step_pattern(_ptr(theta), _ptr(m), _ptr(g), int(d), int(ld),
                                             int(W), int(theta_dtype), int(grad_dtype),
                                             float(beta2), float(lr), stream))
+
+
+def lioncub_probe_panel_pattern(theta, m, g, d, ld, W, theta_dtype, grad_dtype, beta2, lr,
+                                panel_blocks, stream):
+    _check("lioncub_probe_panel_pattern",
+           lib().lioncub_probe_panel_pattern(_ptr(theta), _ptr(m), _ptr(g), int(d), int(ld),
+                                             int(W), int(theta_dtype), int(grad_dtype),
+                                             float(beta2), float(lr), int(panel_blocks), stream))

@@ -75,6 +75,94 @@ __global__ __launch_bounds__(kThreads) void k_pattern(PatternParams p) {
   }
 }
 
+// The same bytes in another arrangement: one workgroup per (block, worker)
+// and the grid worker-major within panels of `panel` consecutive blocks
+// (workgroup k: panel k / (panel*W), then worker, then block), so the
+// workgroups resident together read one worker's rows over a contiguous
+// range; theta is read and written by the workgroup of the last worker.
+// No cross-worker aggregation: this measures what the arrangement streams at.
+template <int TT, int GT>
+__global__ __launch_bounds__(kThreads) void k_panel_pattern(PatternParams p, int panel,
+                                                            int nblk) {
+  const int64_t k = blockIdx.x;
+  const int64_t per_panel = static_cast<int64_t>(panel) * p.W;
+  const int64_t pn = k / per_panel;
+  const int64_t first = pn * panel;
+  const int width = static_cast<int>(nblk - first < panel ? nblk - first : panel);
+  const int64_t r = k - pn * per_panel;
+  const int w = static_cast<int>(r / width);
+  const int64_t b = first + r % width;
+  const int64_t start = b * kBlock;
+  const int len = static_cast<int>(p.d - start < kBlock ? p.d - start : kBlock);
+  int64_t j[kRounds];
+  int nv[kRounds];
+  F4 mv[kRounds], gv[kRounds];
+#pragma unroll
+  for (int q = 0; q < kRounds; ++q) {
+    const int loc = kThreads * kQuad * q + kQuad * static_cast<int>(threadIdx.x);
+    j[q] = start + loc;
+    nv[q] = max(0, min(kQuad, len - loc));
+    if (nv[q] > 0) {
+      const int64_t idx = static_cast<int64_t>(w) * p.ld + j[q];
+      mv[q] = ldnt_f32x4(p.m + idx, nv[q]);
+      gv[q] = ldnt_x4<GT>(p.g, idx, nv[q]);
+    }
+  }
+  uint32_t cnt = 0;
+#pragma unroll
+  for (int q = 0; q < kRounds; ++q) {
+    if (nv[q] == 0) continue;
+    F4 mn;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      mn.v[e] = (p.beta2 * mv[q].v[e]) + (p.omega2 * gv[q].v[e]);
+      cnt += mn.v[e] > 0.0f ? 1u : 0u;
+    }
+    stnt_f32x4(p.m + static_cast<int64_t>(w) * p.ld + j[q], mn, nv[q]);
+  }
+  if (w == p.W - 1) {
+    const float s = 2 * static_cast<int>(cnt) > 16 ? p.lr : -p.lr;
+#pragma unroll
+    for (int q = 0; q < kRounds; ++q) {
+      if (nv[q] == 0) continue;
+      F4 th = ld_x4<TT>(p.theta, j[q], nv[q]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) th.v[e] = th.v[e] - s;
+      stnt_x4<TT>(p.theta, j[q], th, nv[q]);
+    }
+  }
+}
+
+template <int TT, int GT>
+static void launch_panel_t(const PatternParams& p, int panel, hipStream_t st) {
+  const int64_t nblk = (p.d + kBlock - 1) / kBlock;
+  const dim3 g(static_cast<unsigned>(nblk * p.W)), b(kThreads);
+  hipLaunchKernelGGL((k_panel_pattern<TT, GT>), g, b, 0, st, p, panel, static_cast<int>(nblk));
+}
+
+hipError_t launch_panel_pattern(void* theta, float* m, const void* g, int64_t d, int64_t ld, int W,
+                                int theta_bf16, int grad_bf16, float beta2, float lr, int panel,
+                                hipStream_t st) {
+  PatternParams p;
+  p.theta = theta;
+  p.m = m;
+  p.g = g;
+  p.d = d;
+  p.ld = ld;
+  p.W = W;
+  p.beta2 = beta2;
+  p.omega2 = 1.0f - beta2;
+  p.lr = lr;
+  if (theta_bf16) {
+    if (grad_bf16) launch_panel_t<1, 1>(p, panel, st);
+    else launch_panel_t<1, 0>(p, panel, st);
+  } else {
+    if (grad_bf16) launch_panel_t<0, 1>(p, panel, st);
+    else launch_panel_t<0, 0>(p, panel, st);
+  }
+  return hipGetLastError();
+}
+
 template <int TT, int GT>
 static void launch_pattern_t(const PatternParams& p, hipStream_t st) {
   const dim3 g(static_cast<unsigned>((p.d + kBlock - 1) / kBlock)), b(kThreads);

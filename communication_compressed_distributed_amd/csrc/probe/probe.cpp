@@ -12,6 +12,9 @@ hipError_t launch_stream(int kind, const float* a, const float* b, float* c, int
                          hipStream_t st);
 hipError_t launch_pattern(void* theta, float* m, const void* g, int64_t d, int64_t ld, int W,
                           int theta_bf16, int grad_bf16, float beta2, float lr, hipStream_t st);
+hipError_t launch_panel_pattern(void* theta, float* m, const void* g, int64_t d, int64_t ld, int W,
+                                int theta_bf16, int grad_bf16, float beta2, float lr, int panel,
+                                hipStream_t st);
 }  // namespace lioncub
 
 namespace {
@@ -46,6 +49,25 @@ int lioncub_probe_step_pattern(void* theta, float* m, const void* g, int64_t d, 
   return dev_status(lioncub::launch_pattern(theta, m, g, d, ld, W, theta_dtype == LIONCUB_BF16,
                                             grad_dtype == LIONCUB_BF16, beta2, lr,
                                             static_cast<hipStream_t>(hip_stream)));
+}
+
+int lioncub_probe_panel_pattern(void* theta, float* m, const void* g, int64_t d, int64_t ld,
+                                int32_t W, int32_t theta_dtype, int32_t grad_dtype, float beta2,
+                                float lr, int32_t panel_blocks, void* hip_stream) {
+  if (!theta || !m || !g) return LIONCUB_EINVAL;
+  if (d < 1 || ld < d || ld % 64 != 0) return LIONCUB_EINVAL;
+  if (W < 1 || W > 255 || panel_blocks < 1) return LIONCUB_EINVAL;
+  // one workgroup of 256 work-items per (block, worker): the grid's
+  // work-item count must fit 32 bits
+  if ((d + lioncub::kBlock - 1) / lioncub::kBlock * W * lioncub::kThreads > 0xFFFFFFFFll)
+    return LIONCUB_EINVAL;
+  if ((theta_dtype != LIONCUB_F32 && theta_dtype != LIONCUB_BF16) ||
+      (grad_dtype != LIONCUB_F32 && grad_dtype != LIONCUB_BF16))
+    return LIONCUB_EINVAL;
+  if (!aligned16(theta) || !aligned16(m) || !aligned16(g)) return LIONCUB_EALIGN;
+  return dev_status(lioncub::launch_panel_pattern(
+      theta, m, g, d, ld, W, theta_dtype == LIONCUB_BF16, grad_dtype == LIONCUB_BF16, beta2, lr,
+      panel_blocks, static_cast<hipStream_t>(hip_stream)));
 }
 
 }  // extern "C"

@@ -52,6 +52,19 @@ int lioncub_probe_step_pattern(void *theta, float *m, const void *g, int64_t d, 
                                int32_t W, int32_t theta_dtype, int32_t grad_dtype, float beta2,
                                float lr, void *hip_stream);
 
+/* The same bytes in the arrangement the step does not use: one workgroup
+ * per (4096-element block, worker), the grid worker-major within panels of
+ * panel_blocks consecutive blocks (workgroup k: panel k/(panel_blocks*W),
+ * then worker, then block), so the workgroups resident together stream one
+ * worker's rows over a contiguous range, as a plain triad does; theta is
+ * read and written by the last worker's workgroup.  Same arithmetic as
+ * above per worker, but no aggregation across workers (theta moves by +-lr
+ * from the last worker's momenta only): it measures what that arrangement
+ * streams at, not a step.  Arguments as above; panel_blocks >= 1. */
+int lioncub_probe_panel_pattern(void *theta, float *m, const void *g, int64_t d, int64_t ld,
+                                int32_t W, int32_t theta_dtype, int32_t grad_dtype, float beta2,
+                                float lr, int32_t panel_blocks, void *hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -260,3 +260,26 @@ def test_probe_step_pattern_touches_every_element():
         assert np.array_equal(got[:, d:], m_h[:, d:])
         moved = to_host(th) - th_h
         assert np.all((moved != 0))
+
+
+def test_probe_panel_pattern_touches_every_element():
+    """The panel-arrangement probe also reads and writes every element of
+    every worker exactly once (m <- beta2*m + (1-beta2)*g), whatever the
+    panel width, including a short last panel and a ragged last block."""
+    import torch
+
+    from communication_compressed_distributed_amd import _abi, _probe
+    rs = np.random.default_rng(4)
+    for W, d, panel in ((16, 5 * 4096 + 900, 2), (3, 7 * 4096, 4), (8, 2 * 4096 + 64, 64)):
+        ld = (d + 63) // 64 * 64
+        th_h = rs.normal(0, 0.02, d).astype(np.float32)
+        m_h = rs.normal(0, 1e-3, (W, ld)).astype(np.float32)
+        g_h = rs.normal(0, 1e-3, (W, ld)).astype(np.float32)
+        th, m, g = to_dev(th_h), to_dev(m_h), to_dev(g_h)
+        beta2 = np.float32(0.99)
+        _probe.lioncub_probe_panel_pattern(th, m, g, d, ld, W, 0, 0, float(beta2), 1e-4, panel,
+                                           _abi._stream_handle())
+        torch.cuda.synchronize()
+        want = (beta2 * m_h[:, :d]) + ((np.float32(1) - beta2) * g_h[:, :d])
+        assert np.array_equal(to_host(m)[:, :d], want)
+        assert np.all(to_host(th) != th_h)
