@@ -17,8 +17,9 @@
  * mean-|x| inputs, the summation error bound for the rest, invariants, and
  * torch's bf16 conversion.  The fixed order of the mean-|x| tree is a
  * definition of this project (the pages define M1 only as the mean of the
- * absolute values, with no order of summation):
- * beyond the exact-sum cases and the error bound it is parity unpinned.
+ * absolute values, with no order of summation); each level of it is pinned
+ * by a hand-worked case (tests/golden/m1_order.json) whose sum a different
+ * order would change.
  */
 #include "lco.h"
 
@@ -411,7 +412,9 @@ double lco_minf(const float *x, int64_t n) {
  * floor(y) + [u < y - floor(y)], y = (2^(n-1)-1)/max|x| * x in fp64,
  * u = r * 2^-32 for 32 random bits r (lco_sr_u32), clamped.  PARITY PARTLY
  * UNPINNED (the formula is a reading); pinned: integer y, the threshold's
- * direction, the clamp, unbiasedness and the pages' zero-collapse finding. */
+ * direction, the clamp, unbiasedness, the pages' zero-collapse finding, and
+ * which published generator output and half each element draws
+ * (tests/golden/sr_draws.json). */
 int8_t lco_qinf(float c, double minf, int32_t qbits, uint32_t r) {
   int32_t qmax = (1 << (qbits - 1)) - 1;
   if (minf == 0.0) return 0;

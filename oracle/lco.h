@@ -156,9 +156,10 @@ void lco_step_range(const lco_cfg *cfg, int64_t j0, int64_t j1,
  * in place of rounding to nearest:
  *   q = clamp(floor(y) + [u < y - floor(y)], +-Qmax),  y = (Qmax / max|x|) * x
  * in fp64, u uniform in [0, 1) from the counter-based generator below.
- * Pinned: the generator's published first output, exactness of max|x|,
- * integer y (no randomness), unbiasedness E[q] = y, and the pages' claim
- * that on heavy-tailed updates most codes become 0. */
+ * Pinned: the generator's published first outputs, which output and half
+ * an element draws (tuples worked by hand onto those published outputs),
+ * exactness of max|x|, integer y (no randomness), unbiasedness E[q] = y,
+ * and the pages' claim that on heavy-tailed updates most codes become 0. */
 
 /* SplitMix64 (Steele, Lea and Flood, 2014) used as a counter-based
  * generator: the counter-th output of the stream started at `seed`. */
