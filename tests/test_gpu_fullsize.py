@@ -142,6 +142,28 @@ def test_every_element_at_full_size(wl):
     run_every_element(wl, list(range(1, wl.steps + 1)))
 
 
+EXTRA_EVERY_ELEMENT = {
+    # the max-norm stochastic baseline at the flat 350M x 16 shape (n = 4):
+    # its draws depend on t, d, W, i and j, so every element is its own case
+    "flat-350M-w16-linfq4": wls.FLAT_350M_W16_L1Q4.with_(name="flat-350M-w16-linfq4",
+                                                         agg="linf", steps=3),
+    # D-Lion averaging (fractional update (2v - W)/W) on the GPT-2 small list
+    "gpt2-124M-w8-avg": wls.GPT2_124M_W8_VOTE.with_(name="gpt2-124M-w8-avg", agg="avg"),
+    # the 2-bit-result vote (ties give 0) on the 760M list with averaging
+    # every other step
+    "gpt-760M-w8-tiezero-sync2": wls.GPT_760M_W8_VOTE_SYNC.with_(
+        name="gpt-760M-w8-tiezero-sync2", tie="zero", sync_every=2, steps=2),
+}
+
+
+@pytest.mark.parametrize("name", list(EXTRA_EVERY_ELEMENT))
+def test_every_element_other_aggregations(name):
+    """The other aggregation modes at full size, every element and every
+    norm compared after every step."""
+    wl = EXTRA_EVERY_ELEMENT[name]
+    run_every_element(wl, list(range(1, wl.steps + 1)))
+
+
 def test_flat_1M_w4_vote_fullsize():
     run_fullsize(wls.FLAT_1M_W4_VOTE, steps=list(range(1, 11)))
 
