@@ -3,7 +3,8 @@
  * the state with the HIP runtime, run three steps of each aggregation mode
  * through lioncub_step, and compare theta and the momenta bit for bit with
  * the CPU oracle (liblco, test infrastructure) run on host copies; then the
- * p-bit exchange composed of the standalone calls against the fused step.  Also
+ * p-bit exchange composed of the standalone calls against the fused step, and
+ * two cases through the allocation-free lioncub_step_static.  Also
  * checks that argument errors come back as status codes before anything
  * runs.  Prints one line per case and exits non-zero on any mismatch.
  */
@@ -35,7 +36,9 @@ static float rnd(float scale) {
   return (float)((u - 0.5) * 2.0 * scale);
 }
 
-static int run_case(int32_t agg, int32_t qbits, const char *name) {
+/* use_static: step through lioncub_step_static (no context, no workspace:
+ * the library's fixed scratch array) instead of lioncub_step. */
+static int run_case(int32_t agg, int32_t qbits, const char *name, int use_static) {
   const int64_t d = 3 * 4096 + 1000, ld = (d + 63) / 64 * 64;
   const int32_t W = 5;
   const int64_t off[3] = {0, 8192, d};
@@ -122,7 +125,8 @@ static int run_case(int32_t agg, int32_t qbits, const char *name) {
         h_g[(size_t)i * ld + j] = v;
       }
     CHECK_HIP(hipMemcpy(d_g, h_g, nwl * 4, hipMemcpyHostToDevice));
-    st = lioncub_step(ctx, d_theta, (float *)d_m, d_g, t, NULL);
+    st = use_static ? lioncub_step_static(&cfg, NULL, d_theta, (float *)d_m, d_g, t)
+                    : lioncub_step(ctx, d_theta, (float *)d_m, d_g, t, NULL);
     if (st != LIONCUB_OK) { fprintf(stderr, "%s: step %s\n", name, lioncub_strerror(st)); return 1; }
     lco_step(&oc, ld, o_theta, o_m, h_g, t, NULL);
   }
@@ -229,10 +233,12 @@ static int run_exchange(void) {
 int main(void) {
   int fails = 0;
   fails += run_exchange();
-  fails += run_case(LIONCUB_AGG_VOTE, 0, "vote");
-  fails += run_case(LIONCUB_AGG_L1SUM, 4, "l1-sum n=4");
-  fails += run_case(LIONCUB_AGG_AVG, 0, "average");
-  fails += run_case(LIONCUB_AGG_LINFSUM, 3, "max-norm n=3");
+  fails += run_case(LIONCUB_AGG_VOTE, 0, "vote", 0);
+  fails += run_case(LIONCUB_AGG_L1SUM, 4, "l1-sum n=4", 0);
+  fails += run_case(LIONCUB_AGG_AVG, 0, "average", 0);
+  fails += run_case(LIONCUB_AGG_LINFSUM, 3, "max-norm n=3", 0);
+  fails += run_case(LIONCUB_AGG_L1SUM, 8, "allocation-free l1-sum n=8", 1);
+  fails += run_case(LIONCUB_AGG_VOTE, 0, "allocation-free vote", 1);
   printf(fails ? "FAILED\n" : "OK\n");
   return fails;
 }
