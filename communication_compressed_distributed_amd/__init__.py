@@ -5,24 +5,82 @@ data-parallel workers stacked in one GPU's memory: each forms its Lion update
 vector, compresses it to a 0/1 sign bitmap or to L1-quantised n-bit codes,
 the workers are aggregated by majority vote or integer sum, and the global
 sign updates the parameters and each worker's momentum.  `_abi` mirrors the C
-entry points; `LionCub` keeps a context and its workspace together.
+entry points; `LionCub` keeps a context and its workspace together;
+`StaticStep` runs the allocation-free step with the same options.
 """
 from . import _abi, _checks
 from ._abi import (AGG_AVG, AGG_L1SUM, AGG_LINFSUM, AGG_VOTE, BF16, F32, TIE_PARITY, TIE_ZERO,
                    LionCubError, lioncub_apply, lioncub_destroy, lioncub_init, lioncub_pack,
                    lioncub_pack_codes, lioncub_profile_begin, lioncub_profile_end,
-                   lioncub_quant_l1, lioncub_quant_linf, lioncub_set_stream, lioncub_step, lioncub_strerror,
-                   lioncub_unpack_sum, lioncub_unpack_sum_bits, lioncub_vote, lioncub_vote_bits,
-                   lioncub_workspace_bytes,
-                   make_config)
+                   lioncub_quant_l1, lioncub_quant_linf, lioncub_set_stream, lioncub_step,
+                   lioncub_step_static, lioncub_strerror, lioncub_unpack_sum,
+                   lioncub_unpack_sum_bits, lioncub_vote, lioncub_vote_bits,
+                   lioncub_workspace_bytes, make_config)
 
-__all__ = ["LionCub", "LionCubError", "make_config", "lioncub_workspace_bytes", "lioncub_init",
-           "lioncub_set_stream", "lioncub_step", "lioncub_pack", "lioncub_vote",
+__all__ = ["LionCub", "StaticStep", "LionCubError", "make_config", "lioncub_workspace_bytes",
+           "lioncub_init", "lioncub_set_stream", "lioncub_step", "lioncub_step_static",
+           "lioncub_pack", "lioncub_vote",
            "lioncub_quant_l1", "lioncub_quant_linf", "lioncub_vote_bits", "lioncub_apply",
            "lioncub_pack_codes", "lioncub_unpack_sum", "lioncub_unpack_sum_bits",
            "lioncub_profile_begin", "lioncub_profile_end",
            "lioncub_destroy", "lioncub_strerror", "F32", "BF16", "AGG_VOTE", "AGG_L1SUM",
            "AGG_AVG", "AGG_LINFSUM", "TIE_PARITY", "TIE_ZERO"]
+
+
+def _configure(obj, d, W, tensor_offsets, ld, sync_m, sync_every, theta_dtype, grad_dtype, agg,
+               qbits, tie, beta1, beta2, lr, wd, sr_seed):
+    """Validate the Python-level options and set obj.cfg (the lioncub_config
+    and the host arrays it points to), obj.spec (what the host-side tensor
+    checks need) and the plain fields."""
+    aggs = {"vote": AGG_VOTE, "l1": AGG_L1SUM, "avg": AGG_AVG, "linf": AGG_LINFSUM}
+    if agg not in aggs:
+        raise ValueError(f"agg must be one of {sorted(aggs)}, got {agg!r}")
+    for name, val, allowed in (("theta_dtype", theta_dtype, ("f32", "bf16")),
+                               ("grad_dtype", grad_dtype, ("f32", "bf16")),
+                               ("tie", tie, ("parity", "zero"))):
+        if val not in allowed:
+            raise ValueError(f"{name} must be one of {allowed}, got {val!r}")
+    ld = ld if ld is not None else (d + 63) // 64 * 64
+    offs = tensor_offsets if tensor_offsets is not None else [0, d]
+    obj.cfg = make_config(
+        d, ld, W, offs, sync_m=sync_m, sync_every=sync_every,
+        theta_dtype=BF16 if theta_dtype == "bf16" else F32,
+        grad_dtype=BF16 if grad_dtype == "bf16" else F32,
+        agg=aggs[agg], qbits=qbits,
+        tie_mode=TIE_ZERO if tie == "zero" else TIE_PARITY,
+        beta1=beta1, beta2=beta2, lr=lr, wd=wd, sr_seed=sr_seed)
+    obj.d, obj.ld, obj.W, obj.n_tensors = d, ld, W, len(offs) - 1
+    obj.agg, obj.sync_every = agg, sync_every
+    obj.spec = _checks.Spec(d=d, ld=ld, W=W, n_tensors=len(offs) - 1,
+                            theta_dtype=theta_dtype, grad_dtype=grad_dtype, qbits=qbits)
+
+
+class StaticStep:
+    """The allocation-free step (lioncub_step_static) with the same options
+    as LionCub: no context, no workspace and no device memory of its own --
+    the library's fixed scratch array holds the step's tables and partials.
+    For code that may not allocate (e.g. under stream capture).  Each step
+    checks its tensors on the host first; calls that overlap on one GPU race
+    on the shared array."""
+
+    def __init__(self, d, W, tensor_offsets=None, ld=None, sync_m=None, sync_every=1,
+                 theta_dtype="f32", grad_dtype="f32", agg="vote", qbits=0, tie="parity",
+                 beta1=0.9, beta2=0.99, lr=1e-4, wd=0.1, sr_seed=0):
+        _configure(self, d, W, tensor_offsets, ld, sync_m, sync_every, theta_dtype, grad_dtype,
+                   agg, qbits, tie, beta1, beta2, lr, wd, sr_seed)
+        nbytes = lioncub_workspace_bytes(self.cfg)
+        if nbytes == 0:
+            raise LionCubError("lioncub_workspace_bytes", _abi.EINVAL)
+        if nbytes > _abi.STATIC_SCRATCH_BYTES:
+            raise LionCubError("lioncub_step_static", _abi.ESCRATCH)
+
+    def step(self, theta, m, g, t, stream=None):
+        """One step in place on `stream` (a torch.cuda.Stream; default: the
+        current stream of theta's device, which must be the current device)."""
+        import torch
+        _checks.state(self.spec, theta.device, theta, m, g)
+        s = stream if stream is not None else torch.cuda.current_stream(theta.device)
+        lioncub_step_static(self.cfg, _abi._stream_handle(s), theta, m, g, t)
 
 
 class LionCub:
@@ -35,27 +93,8 @@ class LionCub:
                  theta_dtype="f32", grad_dtype="f32", agg="vote", qbits=0, tie="parity",
                  beta1=0.9, beta2=0.99, lr=1e-4, wd=0.1, sr_seed=0, device="cuda", stream=None):
         import torch
-        aggs = {"vote": AGG_VOTE, "l1": AGG_L1SUM, "avg": AGG_AVG, "linf": AGG_LINFSUM}
-        if agg not in aggs:
-            raise ValueError(f"agg must be one of {sorted(aggs)}, got {agg!r}")
-        for name, val, allowed in (("theta_dtype", theta_dtype, ("f32", "bf16")),
-                                   ("grad_dtype", grad_dtype, ("f32", "bf16")),
-                                   ("tie", tie, ("parity", "zero"))):
-            if val not in allowed:
-                raise ValueError(f"{name} must be one of {allowed}, got {val!r}")
-        ld = ld if ld is not None else (d + 63) // 64 * 64
-        offs = tensor_offsets if tensor_offsets is not None else [0, d]
-        self.cfg = make_config(
-            d, ld, W, offs, sync_m=sync_m, sync_every=sync_every,
-            theta_dtype=BF16 if theta_dtype == "bf16" else F32,
-            grad_dtype=BF16 if grad_dtype == "bf16" else F32,
-            agg=aggs[agg], qbits=qbits,
-            tie_mode=TIE_ZERO if tie == "zero" else TIE_PARITY,
-            beta1=beta1, beta2=beta2, lr=lr, wd=wd, sr_seed=sr_seed)
-        self.d, self.ld, self.W, self.n_tensors = d, ld, W, len(offs) - 1
-        self.agg, self.sync_every = agg, sync_every
-        self.spec = _checks.Spec(d=d, ld=ld, W=W, n_tensors=len(offs) - 1,
-                                 theta_dtype=theta_dtype, grad_dtype=grad_dtype, qbits=qbits)
+        _configure(self, d, W, tensor_offsets, ld, sync_m, sync_every, theta_dtype, grad_dtype,
+                   agg, qbits, tie, beta1, beta2, lr, wd, sr_seed)
         nbytes = lioncub_workspace_bytes(self.cfg)
         if nbytes == 0:
             raise LionCubError("lioncub_workspace_bytes", _abi.EINVAL)

@@ -89,3 +89,32 @@ def test_lioncub_rejects_unknown_names_before_allocating(kw):
     from communication_compressed_distributed_amd import LionCub
     with pytest.raises(ValueError):
         LionCub(d=4096, W=2, device="cpu", **kw)
+
+
+def test_static_step_wrapper_checks_before_the_library(monkeypatch):
+    """StaticStep validates its options and the scratch-array size at
+    construction and every tensor before the allocation-free entry point is
+    called (here the entry point is replaced: nothing reaches a device)."""
+    import communication_compressed_distributed_amd as lc
+    from communication_compressed_distributed_amd import _abi
+
+    with pytest.raises(ValueError):
+        lc.StaticStep(d=1000, W=3, agg="sum")
+    with pytest.raises(lc.LionCubError) as e:
+        lc.StaticStep(d=350_000_000, W=128, agg="l1", qbits=4)
+    assert e.value.status == _abi.ESCRATCH
+    st = lc.StaticStep(d=1000, W=3, tensor_offsets=[0, 512, 1000], theta_dtype="bf16", agg="l1",
+                       qbits=4)
+    assert st.ld == 1024 and st.n_tensors == 2
+    calls = []
+    monkeypatch.setattr(lc, "lioncub_step_static", lambda *a: calls.append(a))
+    monkeypatch.setattr(lc._abi, "_stream_handle", lambda s=None: None)
+    monkeypatch.setattr(torch.cuda, "current_stream", lambda dev=None: None)
+    th, m, g = good_state()
+    st.step(th, m, g, 1)
+    assert len(calls) == 1 and calls[0][5] == 1
+    with pytest.raises(ValueError):
+        st.step(th[:999], m, g, 2)
+    with pytest.raises(ValueError):
+        st.step(th, m.t(), g, 2)
+    assert len(calls) == 1

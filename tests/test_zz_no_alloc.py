@@ -97,3 +97,31 @@ def test_static_step_in_a_graph():
         check_float_state(f"graph replay {rep} m", to_host(s_m)[:, : wl.d],
                           to_host(r_m)[:, : wl.d])
     lc.close()
+
+
+def test_static_step_wrapper_matches_context_step():
+    """The checked Python wrapper (StaticStep) over the allocation-free entry
+    point, two steps in a row on one state, against LionCub.step."""
+    import torch
+
+    from communication_compressed_distributed_amd import StaticStep
+    wl = CASES[1]
+    theta, m, _ = _inputs(wl, 1)
+    lc = lioncub_for(wl)
+    st = StaticStep(d=wl.d, W=wl.W, tensor_offsets=wl.offsets, ld=wl.ld,
+                    sync_m=wl.sync_flags if any(wl.sync_flags) else None,
+                    sync_every=wl.sync_every, theta_dtype=wl.theta_dtype,
+                    grad_dtype=wl.grad_dtype, agg=wl.agg, qbits=wl.qbits, tie=wl.tie,
+                    beta1=wl.beta1, beta2=wl.beta2, lr=wl.lr, wd=wl.wd, sr_seed=wl.sr_seed)
+    r_theta, r_m = to_dev(theta), to_dev(m)
+    s_theta, s_m = to_dev(theta), to_dev(m)
+    for t in (1, 2):
+        g = to_dev(gen.host_g(wl, t))
+        lc.step(r_theta, r_m, g, t)
+        st.step(s_theta, s_m, g, t)
+        torch.cuda.synchronize()
+        check_float_state(f"wrapper theta t={t}", to_host(s_theta), to_host(r_theta))
+        check_float_state(f"wrapper m t={t}", to_host(s_m)[:, : wl.d], to_host(r_m)[:, : wl.d])
+    with pytest.raises(ValueError):
+        st.step(s_theta[:-1], s_m, g, 3)
+    lc.close()
