@@ -3,7 +3,8 @@
 // The flat parameter vector is cut into tensors (offsets multiples of 64) and
 // every tensor into blocks of kBlock elements; a block never straddles a
 // tensor, so a workgroup sees one tensor's flags and scales.  The tables live
-// in the caller's workspace, uploaded once at init.
+// in the caller's workspace (or the allocation-free step's fixed array),
+// written by the table kernels of tables.hip.
 #pragma once
 #include <stdint.h>
 
