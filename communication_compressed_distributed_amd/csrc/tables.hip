@@ -7,7 +7,8 @@
 // kernel arguments, kTensChunk entries per launch.  The block and group
 // tables follow from it: block b belongs to the last tensor whose first block
 // id is <= b (every tensor has at least one block, so first block ids rise
-// strictly), and likewise for groups.
+// strictly), and likewise for groups.  A list of at most kTensChunk tensors
+// gets all three tables from one launch.
 #include "ctx.hpp"
 
 namespace lioncub {
@@ -66,6 +67,49 @@ __global__ void k_put_groups(const TensorEnt* __restrict__ tens, int nT, GroupEn
   grp[gq] = ge;
 }
 
+// Every table in one launch when the whole tensor list fits one chunk of
+// kernel arguments: items [0, nT) are tensor entries, [nT, nT + ngrp) groups,
+// the rest blocks; a group or block finds its tensor among the argument
+// entries themselves.  Used on vectors of up to kTensChunk tensors, where the
+// table build is otherwise three launches beside a step that may itself be
+// a few microseconds long.
+__global__ void k_put_tables(TensorChunk c, TensorEnt* __restrict__ tens,
+                             BlockEnt* __restrict__ blk, GroupEnt* __restrict__ grp, int ngrp,
+                             int nblk) {
+  const int64_t k = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int nT = c.count;
+  if (k < nT) {
+    tens[k] = c.ent[k];
+    return;
+  }
+  if (k < nT + ngrp) {
+    const int gq = static_cast<int>(k - nT);
+    int T = 0;
+    while (T + 1 < nT && c.ent[T + 1].grp0 <= gq) ++T;
+    const TensorEnt& te = c.ent[T];
+    const int r = gq - te.grp0;
+    GroupEnt ge;
+    ge.tensor = T;
+    ge.blk = te.blk0 + r * kGroup;
+    ge.cnt = te.nblk - r * kGroup < kGroup ? te.nblk - r * kGroup : kGroup;
+    ge.pad = 0;
+    grp[gq] = ge;
+    return;
+  }
+  if (k < static_cast<int64_t>(nT) + ngrp + nblk) {
+    const int b = static_cast<int>(k - nT - ngrp);
+    int T = 0;
+    while (T + 1 < nT && c.ent[T + 1].blk0 <= b) ++T;
+    const TensorEnt& te = c.ent[T];
+    const int64_t s = static_cast<int64_t>(b - te.blk0) * kBlock;
+    BlockEnt be;
+    be.start = te.off + s;
+    be.len = static_cast<int32_t>(te.n - s < kBlock ? te.n - s : kBlock);
+    be.tensor = T;
+    blk[b] = be;
+  }
+}
+
 hipError_t build_tables(const lioncub_config* c, int64_t nblk, int64_t ngrp, TensorEnt* tens,
                         BlockEnt* blk, GroupEnt* grp, int32_t* any_sync, hipStream_t st) {
   TensorChunk ch;
@@ -88,12 +132,19 @@ hipError_t build_tables(const lioncub_config* c, int64_t nblk, int64_t ngrp, Ten
       grp0 += te.ngrp;
       sync |= te.sync;
     }
+    if (c->n_tensors <= kTensChunk) break;  // one chunk: all tables in one launch below
     hipLaunchKernelGGL(k_put_tensors, dim3(1), dim3(kTensChunk), 0, st, ch, tens);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (blk0 != nblk || grp0 != ngrp) return hipErrorInvalidValue;  // checked config: cannot happen
   *any_sync = sync;
+  if (c->n_tensors <= kTensChunk) {
+    const int64_t items = c->n_tensors + ngrp + nblk;
+    hipLaunchKernelGGL(k_put_tables, dim3(static_cast<unsigned>((items + 255) / 256)), dim3(256),
+                       0, st, ch, tens, blk, grp, static_cast<int>(ngrp), static_cast<int>(nblk));
+    return hipGetLastError();
+  }
   const unsigned nb = static_cast<unsigned>((nblk + 255) / 256);
   hipLaunchKernelGGL(k_put_blocks, dim3(nb), dim3(256), 0, st, tens, c->n_tensors, blk,
                      static_cast<int>(nblk));
