@@ -198,6 +198,32 @@ def test_quant_l1_handworked():
     _quant_case(x, [("a", 5)], 3)
 
 
+def test_fp32_evaluation_order_handworked_gpu():
+    """The library's theta and averaged-momentum arithmetic against values
+    worked by hand where another evaluation order or a fused multiply-add
+    would round differently (tests/golden/fp32_order.json), not against the
+    oracle."""
+    import torch
+
+    from tests.test_oracle_pins import fp32_order_average_run, fp32_order_theta_run
+
+    def step(wl, theta, m, g, want_m=False):
+        lc = lioncub_for(wl)
+        th = to_dev(theta if theta is not None else np.zeros(wl.d, np.float32))
+        dm = to_dev(m)
+        lc.step(th, dm, to_dev(g), 1)
+        torch.cuda.synchronize()
+        lc.close()
+        return to_host(dm) if want_m else to_host(th)
+
+    gd = golden("fp32_order.json")
+    for case in gd["theta_cases"]:
+        assert np.all(fp32_order_theta_run(step, case) == int(case["theta_next_hex"], 16)), \
+            case["name"]
+    want = np.array([int(h, 16) for h in gd["average_case"]["m_next_hex"]], np.uint32)
+    assert np.all(fp32_order_average_run(step) == want[None, :])
+
+
 def _m1_order_rows(cases, W):
     """The hand-worked summation-order cases as consecutive tensors; worker
     i holds the case vectors scaled by (-2)^i (exact at every tree level)."""

@@ -218,6 +218,59 @@ def test_sign_flip_step_closed_form(oracle):
     np.testing.assert_allclose(m[0], mT, atol=2e-6)
 
 
+def _f32(hexstr):
+    return float(np.array([int(hexstr, 16)], np.uint32).view(np.float32)[0])
+
+
+def fp32_order_theta_run(step, case):
+    """One vote step of a single worker with c > 0 (s = +1) on a 64-element
+    vector holding the case's theta; returns theta' as fp32 bit patterns."""
+    wl = one_tensor(64, 1, lr=_f32(case["lr_hex"]), wd=_f32(case["wd_hex"]))
+    theta = np.full(64, _f32(case["theta_hex"]), np.float32)
+    m = np.zeros((1, wl.ld), np.float32)
+    g = np.zeros((1, wl.ld), np.float32)
+    g[:, :64] = 1.0                      # c = (1 - beta1) > 0 everywhere
+    return step(wl, theta, m, g).view(np.uint32)
+
+
+def fp32_order_average_run(step):
+    """One averaging step of three workers (beta2 = 1/2, g = 0) on the
+    fixture's two columns; returns m' as fp32 bit patterns [3][2]."""
+    case = golden("fp32_order.json")["average_case"]
+    wl = wls.Workload(name="avgorder", tensors=[("wte", 64)], W=case["W"], beta2=case["beta2"],
+                      sync_names=("wte",), sync_every=1)
+    m = np.zeros((wl.W, wl.ld), np.float32)
+    m[:, :2] = np.array(case["m"], np.float32)
+    g = np.zeros((wl.W, wl.ld), np.float32)
+    return step(wl, None, m, g, want_m=True)[:, :2].view(np.uint32)
+
+
+def test_fp32_evaluation_order_handworked(oracle):
+    """The written order of theta' = theta - (lr*(s + wd*theta)) with one
+    rounding per operation and no fused multiply-add, and the worker-order
+    fp32 sum of the averaged momenta divided by W, against values worked by
+    hand where another order or a contraction would round differently
+    (tests/golden/fp32_order.json)."""
+    gd = golden("fp32_order.json")
+
+    def step(wl, theta, m, g, want_m=False):
+        th = theta if theta is not None else np.zeros(wl.d, np.float32)
+        oracle.step(wl, th, m, g, 1)
+        return m if want_m else th
+
+    for case in gd["theta_cases"]:
+        want = int(case["theta_next_hex"], 16)
+        for alt in case["alternatives"].values():
+            assert int(alt, 16) != want
+        assert np.all(fp32_order_theta_run(step, case) == want), case["name"]
+    av = gd["average_case"]
+    want = [int(h, 16) for h in av["m_next_hex"]]
+    got = fp32_order_average_run(step)
+    assert np.all(got == np.array(want, np.uint32)[None, :])
+    for alt in av["alternatives"].values():
+        assert int(alt, 16) not in want
+
+
 def test_bf16_theta_one_ulp_of_closed_form(oracle):
     """bf16 parameters: the widened value follows the same closed form to
     within one bf16 ulp per step (the step is computed in fp32, then rounded
