@@ -5,6 +5,8 @@ tie rules, fp32/bf16 theta and gradients, momentum sync on random tensors
 and intervals, row padding, random step indices.  Each configuration runs
 two steps with the debug outputs and one production step; everything is
 compared bit for bit."""
+import os
+
 import numpy as np
 import pytest
 
@@ -15,7 +17,10 @@ from tests.harness import gpu_step_vs_oracle
 
 pytestmark = pytest.mark.gpu
 
-N_CONFIGS = 100
+# configurations k = FIRST .. FIRST + N - 1 (the environment can widen the
+# sweep for a longer run; the default suite runs the first 100)
+N_CONFIGS = int(os.environ.get("LIONCUB_RANDOM_CONFIGS", "100"))
+FIRST_CONFIG = int(os.environ.get("LIONCUB_RANDOM_FIRST", "0"))
 
 
 def random_workload(k):
@@ -47,7 +52,7 @@ def random_workload(k):
         g_tensor_scale=(1e-4, 1e-2) if rs.random() < 0.5 else None)
 
 
-@pytest.mark.parametrize("k", range(N_CONFIGS))
+@pytest.mark.parametrize("k", range(FIRST_CONFIG, FIRST_CONFIG + N_CONFIGS))
 def test_random_config(k):
     wl = random_workload(k)
     t0 = int(np.random.default_rng(k).integers(1, 1000))
