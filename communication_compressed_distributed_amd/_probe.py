@@ -15,6 +15,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "liblioncub_probe.so")
 
 PROBE_READ, PROBE_COPY, PROBE_TRIAD = 0, 1, 2
+PROBE_CACHED, PROBE_MASKED = 1, 2     # lioncub_probe_step_pattern flags
 EXPORTS = ["lioncub_probe_stream", "lioncub_probe_step_pattern", "lioncub_probe_panel_pattern"]
 
 _lib = None
@@ -30,7 +31,7 @@ def lib():
         L.lioncub_probe_stream.argtypes = [i32, vp, vp, vp, i64, vp]
         L.lioncub_probe_stream.restype = C.c_int
         L.lioncub_probe_step_pattern.argtypes = [vp, vp, vp, i64, i64, i32, i32, i32, C.c_float,
-                                                 C.c_float, vp]
+                                                 C.c_float, i32, vp]
         L.lioncub_probe_step_pattern.restype = C.c_int
         L.lioncub_probe_panel_pattern.argtypes = [vp, vp, vp, i64, i64, i32, i32, i32, C.c_float,
                                                   C.c_float, i32, vp]
@@ -49,11 +50,12 @@ def lioncub_probe_stream(kind, a, b, c, n, stream):
            lib().lioncub_probe_stream(int(kind), _ptr(a), _ptr(b), _ptr(c), int(n), stream))
 
 
-def lioncub_probe_step_pattern(theta, m, g, d, ld, W, theta_dtype, grad_dtype, beta2, lr, stream):
+def lioncub_probe_step_pattern(theta, m, g, d, ld, W, theta_dtype, grad_dtype, beta2, lr, stream,
+                               flags=0):
     _check("lioncub_probe_step_pattern",
            lib().lioncub_probe_step_pattern(_ptr(theta), _ptr(m), _ptr(g), int(d), int(ld),
                                             int(W), int(theta_dtype), int(grad_dtype),
-                                            float(beta2), float(lr), stream))
+                                            float(beta2), float(lr), int(flags), stream))
 
 
 def lioncub_probe_panel_pattern(theta, m, g, d, ld, W, theta_dtype, grad_dtype, beta2, lr,

@@ -11,7 +11,8 @@ namespace lioncub {
 hipError_t launch_stream(int kind, const float* a, const float* b, float* c, int64_t n,
                          hipStream_t st);
 hipError_t launch_pattern(void* theta, float* m, const void* g, int64_t d, int64_t ld, int W,
-                          int theta_bf16, int grad_bf16, float beta2, float lr, hipStream_t st);
+                          int theta_bf16, int grad_bf16, float beta2, float lr, int flags,
+                          hipStream_t st);
 hipError_t launch_panel_pattern(void* theta, float* m, const void* g, int64_t d, int64_t ld, int W,
                                 int theta_bf16, int grad_bf16, float beta2, float lr, int panel,
                                 hipStream_t st);
@@ -37,7 +38,7 @@ int lioncub_probe_stream(int32_t kind, const float* a, const float* b, float* c,
 
 int lioncub_probe_step_pattern(void* theta, float* m, const void* g, int64_t d, int64_t ld,
                                int32_t W, int32_t theta_dtype, int32_t grad_dtype, float beta2,
-                               float lr, void* hip_stream) {
+                               float lr, int32_t flags, void* hip_stream) {
   if (!theta || !m || !g) return LIONCUB_EINVAL;
   if (d < 1 || ld < d || ld % 64 != 0 || (d + lioncub::kBlock - 1) / lioncub::kBlock > 0x7FFFFFFF)
     return LIONCUB_EINVAL;
@@ -46,8 +47,13 @@ int lioncub_probe_step_pattern(void* theta, float* m, const void* g, int64_t d, 
       (grad_dtype != LIONCUB_F32 && grad_dtype != LIONCUB_BF16))
     return LIONCUB_EINVAL;
   if (!aligned16(theta) || !aligned16(m) || !aligned16(g)) return LIONCUB_EALIGN;
+  const int32_t shaping = LIONCUB_PROBE_CAP_MASK | LIONCUB_PROBE_DRAIN_MASK;
+  if (flags & ~(LIONCUB_PROBE_CACHED | LIONCUB_PROBE_MASKED | shaping)) return LIONCUB_EINVAL;
+  if ((flags & shaping) && (flags & (LIONCUB_PROBE_CACHED | LIONCUB_PROBE_MASKED)))
+    return LIONCUB_EINVAL;
+  if ((flags & LIONCUB_PROBE_CAP_MASK) && (flags & LIONCUB_PROBE_DRAIN_MASK)) return LIONCUB_EINVAL;
   return dev_status(lioncub::launch_pattern(theta, m, g, d, ld, W, theta_dtype == LIONCUB_BF16,
-                                            grad_dtype == LIONCUB_BF16, beta2, lr,
+                                            grad_dtype == LIONCUB_BF16, beta2, lr, flags,
                                             static_cast<hipStream_t>(hip_stream)));
 }
 

@@ -47,10 +47,37 @@ int lioncub_probe_stream(int32_t kind, const float *a, const float *b, float *c,
  *   theta: device [d] fp32 or bf16 per theta_dtype (read, written)
  *   m:     device [W][ld] fp32 (read, written)
  *   g:     device [W][ld] fp32 or bf16 per grad_dtype (read)
- *   d >= 1, ld >= d and a multiple of 64, W in 1..255. */
+ *   d >= 1, ld >= d and a multiple of 64, W in 1..255.
+ *   flags: 0, or any of
+ *     LIONCUB_PROBE_CACHED: plain loads and stores instead of nontemporal
+ *       ones (a working set smaller than the last-level cache can then stay
+ *       there from one call to the next);
+ *     LIONCUB_PROBE_MASKED: every block takes the per-lane predicated path
+ *       the step kernel uses only for a ragged last block (the same bytes;
+ *       its generated code waits for a wave's loads before each new quad,
+ *       so about two are in flight per wave);
+ *     LIONCUB_PROBE_CAP2 / _CAP4 / _CAP8 (not with the two above): the
+ *       full-block path with at most 2, 4 or 8 vector-memory operations of
+ *       a wave in flight while a batch's loads are issued;
+ *     LIONCUB_PROBE_DRAIN_BATCH / _DRAIN_QUAD / _SERIAL (alone): the
+ *       full-block path with the wave waiting for all its memory operations
+ *       (stores included) before each batch's loads, before each quad's
+ *       pair of loads, or before each pair of loads and each store. */
+enum {
+  LIONCUB_PROBE_CACHED = 1,
+  LIONCUB_PROBE_MASKED = 2,
+  LIONCUB_PROBE_CAP2 = 4,
+  LIONCUB_PROBE_CAP4 = 8,
+  LIONCUB_PROBE_CAP8 = 12,
+  LIONCUB_PROBE_CAP_MASK = 12,
+  LIONCUB_PROBE_DRAIN_BATCH = 16,
+  LIONCUB_PROBE_DRAIN_QUAD = 32,
+  LIONCUB_PROBE_SERIAL = 48,
+  LIONCUB_PROBE_DRAIN_MASK = 48
+};
 int lioncub_probe_step_pattern(void *theta, float *m, const void *g, int64_t d, int64_t ld,
                                int32_t W, int32_t theta_dtype, int32_t grad_dtype, float beta2,
-                               float lr, void *hip_stream);
+                               float lr, int32_t flags, void *hip_stream);
 
 /* The same bytes in the arrangement the step does not use: one workgroup
  * per (4096-element block, worker), the grid worker-major within panels of

@@ -238,7 +238,11 @@ def test_probe_step_pattern_touches_every_element():
 
     from communication_compressed_distributed_amd import _abi, _probe
     rs = np.random.default_rng(3)
-    for W, d, gd in ((16, 5 * 4096 + 900, 0), (5, 4096 + 64, 1), (8, 3 * 4096, 1)):
+    for W, d, gd, flags in ((16, 5 * 4096 + 900, 0, 0), (5, 4096 + 64, 1, 0), (8, 3 * 4096, 1, 1),
+                            (4, 2 * 4096 + 36, 0, 1), (16, 3 * 4096 + 100, 0, 2), (5, 2 * 4096, 1, 3),
+                            (16, 3 * 4096 + 64, 0, 4), (3, 2 * 4096 + 8, 1, 8), (8, 4096, 0, 12),
+                            (7, 3 * 4096 + 4, 0, 16), (16, 2 * 4096 + 12, 1, 32),
+                            (2, 4 * 4096 + 2000, 0, 48)):
         ld = (d + 63) // 64 * 64 + 64
         th_h = rs.normal(0, 0.02, d).astype(np.float32)
         m_h = rs.normal(0, 1e-3, (W, ld)).astype(np.float32)
@@ -252,7 +256,7 @@ def test_probe_step_pattern_touches_every_element():
             gw = g32
         beta2, lr = np.float32(0.99), np.float32(1e-4)
         _probe.lioncub_probe_step_pattern(th, m, g, d, ld, W, 0, gd, float(beta2), float(lr),
-                                          _abi._stream_handle())
+                                          _abi._stream_handle(), flags=flags)
         torch.cuda.synchronize()
         want = (beta2 * m_h[:, :d]) + ((np.float32(1) - beta2) * gw[:, :d])
         got = to_host(m)

@@ -35,12 +35,16 @@ def test_probe_stream_rejects_bad_arguments_before_device():
 def test_probe_pattern_rejects_bad_arguments_before_device():
     L = _probe.lib()
     p = C.c_void_p(256)
-    ok = dict(d=5000, ld=5056, W=4, td=0, gd=0)
+    ok = dict(d=5000, ld=5056, W=4, td=0, gd=0, flags=0)
 
     def call(theta=p, m=p, g=p, **kw):
         a = dict(ok, **kw)
         return L.lioncub_probe_step_pattern(theta, m, g, a["d"], a["ld"], a["W"], a["td"], a["gd"],
-                                            0.99, 1e-4, None)
+                                            0.99, 1e-4, a["flags"], None)
+    assert call(flags=64) == _abi.EINVAL                 # unknown bit
+    assert call(flags=1 | 4) == _abi.EINVAL              # cap with plain accesses
+    assert call(flags=2 | 16) == _abi.EINVAL             # drain with the masked path
+    assert call(flags=4 | 16) == _abi.EINVAL             # cap and drain together
     assert call(theta=None) == _abi.EINVAL
     assert call(d=0) == _abi.EINVAL
     assert call(ld=5000) == _abi.EINVAL                  # not a multiple of 64
