@@ -485,7 +485,7 @@ const char* lioncub_strerror(int status) {
     case LIONCUB_EALIGN: return "pointer not aligned as required";
     case LIONCUB_EWORKSPACE: return "workspace missing, misaligned or too small";
     case LIONCUB_EDEVICE: return "HIP runtime or kernel launch failure";
-    case LIONCUB_EUNSUPPORTED: return "configuration not supported by this build";
+    case LIONCUB_EUNSUPPORTED: return "configuration not supported by this library";
     case LIONCUB_ENOMEM: return "out of host memory";
     case LIONCUB_ESCRATCH:
       return "configuration needs more than the library's fixed scratch array";

@@ -62,7 +62,7 @@ enum {
   LIONCUB_EALIGN = -2,       /* pointer not aligned as required           */
   LIONCUB_EWORKSPACE = -3,   /* workspace missing, misaligned or too small */
   LIONCUB_EDEVICE = -4,      /* HIP runtime / launch failure              */
-  LIONCUB_EUNSUPPORTED = -5, /* valid request this build does not support */
+  LIONCUB_EUNSUPPORTED = -5, /* valid request this library does not support */
   LIONCUB_ENOMEM = -6,       /* host memory for the context or its
                                 profiling events could not be allocated   */
   LIONCUB_ESCRATCH = -7      /* lioncub_step_static: the configuration
