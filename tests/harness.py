@@ -98,6 +98,41 @@ def zero_device_m(d_m, wl, zeros):
         d_m[i, a:b] = 0
 
 
+def gpu_step_fn():
+    """One library step on device copies of host inputs, returning the new
+    state and every debug output as host arrays (the same keys as the
+    oracle's step), so a hand-worked check can run on the library directly."""
+    import torch
+
+    def step(wl, theta, m, g, t):
+        tb, gb = wl.theta_dtype == "bf16", wl.grad_dtype == "bf16"
+        lc = lioncub_for(wl.with_(ld_pad=m.shape[1] - wl.ld))
+        d_theta, d_m, d_g = to_dev(theta, tb), to_dev(m), to_dev(g, gb)
+        dbg = {"sign": torch.zeros(wl.d, dtype=torch.int8, device="cuda"),
+               "stats": torch.full((wl.n_tensors, 4), -1, dtype=torch.int64, device="cuda"),
+               "mvar_max": torch.full((wl.n_tensors,), -1.0, dtype=torch.float64, device="cuda")}
+        if wl.agg in ("vote", "avg"):
+            dbg["bits"] = torch.full((wl.W, m.shape[1] // 64), -1, dtype=torch.int64, device="cuda")
+            dbg["counts"] = torch.zeros(wl.d, dtype=torch.uint8, device="cuda")
+        else:
+            dbg["codes"] = torch.zeros((wl.W, m.shape[1]), dtype=torch.int8, device="cuda")
+            dbg["sums"] = torch.zeros(wl.d, dtype=torch.int32, device="cuda")
+            dbg["m1"] = torch.zeros((wl.W, wl.n_tensors), dtype=torch.float64, device="cuda")
+        lc.step(d_theta, d_m, d_g, t, dbg)
+        torch.cuda.synchronize()
+        lc.close()
+        out = {k: to_host(v) for k, v in dbg.items()}
+        out["stats"] = out["stats"].view(np.uint64)
+        if "bits" in out:
+            out["bits"] = out["bits"].view(np.uint64)
+        out["theta"] = to_host(d_theta)
+        if tb:
+            out["theta"] = out["theta"].view(np.uint16)
+        out["m"] = to_host(d_m)
+        return out
+    return step
+
+
 def gpu_step_vs_oracle(wl, steps=2, t0=1, zeros=True, debug=True, seed_shift=0):
     """Run `steps` steps on both sides from the same seeded state; compare
     everything after every step.  Each side carries its own theta and m from

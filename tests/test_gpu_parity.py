@@ -9,7 +9,7 @@ import pytest
 from oracle import lco
 from synth import workloads as wls
 from tests.conftest import golden
-from tests.harness import gpu_step_vs_oracle, lioncub_for, to_dev, to_host
+from tests.harness import gpu_step_fn, gpu_step_vs_oracle, lioncub_for, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -222,6 +222,58 @@ def test_fp32_evaluation_order_handworked_gpu():
             case["name"]
     want = np.array([int(h, 16) for h in gd["average_case"]["m_next_hex"]], np.uint32)
     assert np.all(fp32_order_average_run(step) == want[None, :])
+
+
+@pytest.mark.parametrize("t", [1, 2])
+def test_tie_rule_handworked_gpu(t):
+    """Both tie rules on columns that tie by construction: applied sign,
+    theta and the diagnostics' counts against values fixed by hand."""
+    from tests.test_oracle_pins import tie_rule_run
+    tie_rule_run(gpu_step_fn(), t)
+
+
+def test_bf16_theta_decay_handworked_gpu():
+    from tests.test_oracle_pins import bf16_decay_run
+    bf16_decay_run(gpu_step_fn())
+
+
+def test_identical_momenta_zero_spread_gpu():
+    """64 identical workers: the largest inter-worker variance is exactly 0
+    although its fp64 evaluation is negative for some columns."""
+    from tests.test_oracle_pins import zero_spread_run
+    zero_spread_run(gpu_step_fn())
+
+
+def test_quant_l1_scale_precision_gpu():
+    """Eq. (1) on a row whose first code sits 1.65e-8 below a rounding
+    boundary, worked in exact arithmetic: the standalone quantiser and the
+    fused step's codes (c = x with beta1 = 1/2, m = 0, g = 2x)."""
+    import torch
+
+    from tests.test_oracle_pins import scale_precision_run
+
+    def standalone(x, n):
+        wl = wls.flat("sp", x.size, W=1, agg="l1", qbits=n)
+        xx = np.zeros((1, wl.ld), np.float32)
+        xx[0, : x.size] = x
+        lc = lioncub_for(wl)
+        codes = torch.zeros((1, wl.ld), dtype=torch.int8, device="cuda")
+        m1 = torch.zeros((1, 1), dtype=torch.float64, device="cuda")
+        lc.quant_l1(to_dev(xx), codes, m1)
+        torch.cuda.synchronize()
+        lc.close()
+        return to_host(codes)[0, : x.size], float(to_host(m1)[0, 0])
+
+    def fused(x, n):
+        wl = wls.flat("sp", x.size, W=1, agg="l1", qbits=n, beta1=0.5)
+        g = np.zeros((1, wl.ld), np.float32)
+        g[0, : x.size] = np.float32(2) * x
+        out = gpu_step_fn()(wl, np.zeros(x.size, np.float32), np.zeros((1, wl.ld), np.float32),
+                            g, 1)
+        return out["codes"][0, : x.size], float(out["m1"][0, 0])
+
+    scale_precision_run(standalone)
+    scale_precision_run(fused)
 
 
 def _m1_order_rows(cases, W):

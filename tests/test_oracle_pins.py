@@ -49,6 +49,18 @@ def test_bf16_rounding_matches_torch(oracle):
     assert L.lco_bf16_to_f32(0x3F80) == 1.0
 
 
+def test_bf16_nan_stays_nan(oracle):
+    """Every fp32 NaN, whatever its sign and payload, becomes a bf16 NaN
+    (exponent all ones, mantissa not zero): dropping the low 16 bits would
+    turn a NaN whose payload lies only there into an infinity.  Which NaN is
+    the reading of this library (the canonical quiet 0x7FC0, on both sides)."""
+    pats = np.array([0x7F800001, 0xFF800001, 0x7F80FFFF, 0x7FA00000, 0xFFC00000,
+                     0x7FFFFFFF, 0xFFFFFFFF, 0x7FC00001], dtype=np.uint32)
+    got = oracle.f32_to_bf16(pats.view(np.float32))
+    assert np.all((got & 0x7F80) == 0x7F80) and np.all((got & 0x007F) != 0)
+    assert np.all(got == 0x7FC0)
+
+
 # ------------------------------------------------------ 1-bit compression --
 
 def test_bit_rule_zero_parity(oracle):
@@ -294,6 +306,25 @@ def test_bf16_theta_one_ulp_of_closed_form(oracle):
     assert np.all(np.abs(got - want) <= ulp * 0.5 + 1e-12)
 
 
+def bf16_decay_run(step):
+    """bf16 parameters, exact by hand: lr = 2^-4, wd = 1, W = 1, m = 0,
+    g = (+1e-3, -1e-3) so the signs are (+1, -1):
+      theta = 1:  1 - 2^-4 (1 + 1)    = 0.875
+      theta = -2: -2 - 2^-4 (-1 - 2)  = -1.8125
+    both exact in bf16 (without the wd*theta term: 0.9375 and -1.9375)."""
+    from synth.gen import to_bf16_bits
+    wl = one_tensor(2, 1, theta_dtype="bf16", grad_dtype="bf16", lr=2.0 ** -4, wd=1.0)
+    theta = to_bf16_bits(np.array([1.0, -2.0], np.float32))
+    g = np.zeros((1, 64), np.uint16)
+    g[0, :2] = to_bf16_bits(np.array([1e-3, -1e-3], np.float32))
+    out = step(wl, theta, np.zeros((1, 64), np.float32), g, 1)
+    assert bf16_bits_to_f32(out["theta"]).tolist() == [0.875, -1.8125]
+
+
+def test_bf16_theta_decay_handworked(oracle):
+    bf16_decay_run(oracle_step_fn(oracle))
+
+
 # ------------------------------------------------------ L1 quantisation ----
 
 def _quant_one(oracle, x, n):
@@ -358,6 +389,29 @@ def test_quant_l1_exact_rational(oracle, n):
                 frac = y - math.floor(y)
                 near_half = abs(frac - Fraction(1, 2)) <= abs(y) * Fraction(1, 2**48)
                 assert near_half and abs(q - want) == 1 and abs(q) <= qmax, (x, y, q, want)
+
+
+def scale_precision_run(quant):
+    """Eq. (1) on the row x = [v, w] (fp32 bits 0x3e042098, 0x405ef701,
+    found by a search over rows whose first code sits close to a rounding
+    boundary): M1 = (v + w)/2 exactly, and Qmax*v/M1 is 1/2 - 1.65e-8 in
+    exact arithmetic, so Q1(v) = 0 at n = 4; a scale Qmax/M1 rounded to fp32
+    (relative error up to 2^-24) moves the product above 1/2 and gives 1.
+    The expected codes are computed here in exact rational arithmetic.
+    `quant(x, n)` returns (codes, M1) of the one-row, one-tensor vector x."""
+    x = np.array([0x3E042098, 0x405EF701], dtype=np.uint32).view(np.float32)
+    codes, M = quant(x, 4)
+    Mx = (Fraction(float(x[0])) + Fraction(float(x[1]))) / 2
+    assert M == float(Mx)
+    ys = [Fraction(float(v)) * 7 / Mx for v in x]
+    assert Fraction(1, 2) - ys[0] > Fraction(1, 2**27)         # near, but not at, 1/2
+    want = [max(-7, min(7, _nearest_even(y))) for y in ys]
+    assert want == [0, 7]
+    assert list(codes) == want
+
+
+def test_quant_l1_scale_is_not_rounded_to_fp32(oracle):
+    scale_precision_run(lambda x, n: _quant_one(oracle, x, n))
 
 
 def test_quant_l1_invariants(oracle):
@@ -631,8 +685,47 @@ def test_vote_bits_decode_to_vote_sign(oracle, W, tie):
             dec = np.where(zer[:d] == 1, 0, np.where(pos[:d] == 1, 1, -1))
             assert np.array_equal(dec, sign)
             assert not pos[d:].any() and not zer[d:].any()
+            assert not (pos & zer).any()                 # bit 1 means +1, and a zero is not +1
             if tm == oracle.TIE_PARITY:
                 assert not zer.any()
+
+
+def oracle_step_fn(oracle):
+    """One whole oracle step on copies of the inputs, returning the new state
+    and every debug output; the GPU tests pass a function of the same shape
+    backed by the library, so the hand-worked checks below run on both."""
+    def step(wl, theta, m, g, t):
+        theta, m = theta.copy(), m.copy()
+        out = oracle.step(wl, theta, m, g.copy(), t, debug=True)
+        out.update(theta=theta, m=m)
+        return out
+    return step
+
+
+def tie_rule_run(step, t):
+    """W = 2 workers with opposite signs at every element tie the vote.
+    With TIE_ZERO the applied sign is 0, and with no weight decay theta does
+    not move; with TIE_PARITY a tie takes the exact-zero rule, +1 on odd and
+    -1 on even steps, so theta moves by -lr or +lr.  The diagnostics count
+    each column once as a tie and, under TIE_ZERO, once as a zero sign,
+    never as a match or flip: the sum of c is 0 there (c = +-g/2 exactly)."""
+    W, d = 2, 200
+    g = np.zeros((W, 256), np.float32)
+    g[0, :d] = 0.25
+    g[1, :d] = -0.25
+    theta0 = np.linspace(-1, 1, d).astype(np.float32)
+    for tie in ("zero", "parity"):
+        wl = wls.flat("tie", d, W=W, beta1=0.5, wd=0.0, lr=2.0 ** -10, tie=tie)
+        out = step(wl, theta0, np.zeros((W, 256), np.float32), g, t)
+        s = 0 if tie == "zero" else (1 if t % 2 else -1)
+        assert np.all(out["sign"] == s), tie
+        assert np.array_equal(out["theta"], theta0 - np.float32(2.0 ** -10) * np.float32(s)), tie
+        assert out["stats"][0].tolist() == [d, 0, 0, d if tie == "zero" else 0], tie
+
+
+@pytest.mark.parametrize("t", [1, 2])
+def test_step_tie_rule(oracle, t):
+    tie_rule_run(oracle_step_fn(oracle), t)
 
 
 def test_apply_closed_form(oracle):
@@ -827,6 +920,27 @@ def test_stats_momentum_variance_exact(oracle):
             mean = sum(vals) / W
             best = max(best, sum((v - mean) ** 2 for v in vals) / W)
         assert dbg["mvar_max"][T] == float(best)
+
+
+def zero_spread_run(step):
+    """W = 64 identical workers: every new momentum of a column is the same
+    value, so the inter-worker variance is 0.  Summed in fp64 in worker
+    order, 64 squares need more than 53 bits and S2/W - (S1/W)^2 comes out
+    as about -1e-15 for many values (0.8125477, fp32 0x3f500321, among
+    them); the spread is the variance floored at 0, so its maximum is 0."""
+    W, d = 64, 4096
+    rs = np.random.default_rng(6)
+    wl = wls.flat("mv0", d, W=W, beta2=0.5)
+    v = rs.uniform(0.5, 1.0, d).astype(np.float32)
+    v[0] = np.array([0x3F500321], np.uint32).view(np.float32)[0]
+    g = np.tile(np.float32(2) * v, (W, 1))             # m' = g/2 = v exactly (beta2 = 1/2, m = 0)
+    out = step(wl, np.zeros(d, np.float32), np.zeros((W, d), np.float32), g, 1)
+    assert np.array_equal(out["m"][:, :d], np.tile(v, (W, 1)))
+    assert out["mvar_max"][0] == 0.0
+
+
+def test_stats_identical_momenta_have_zero_spread(oracle):
+    zero_spread_run(oracle_step_fn(oracle))
 
 
 # ----------------------------------- max-norm stochastic baseline (Q-inf) --
