@@ -42,7 +42,8 @@
  *    overlap.  A context is not thread-safe; many contexts may coexist.
  *  - Floating point is IEEE round-to-nearest-even, one operation at a time,
  *    no fused multiply-add contraction, subnormals kept.  bf16 values are
- *    widened exactly and narrowed round-to-nearest-even.
+ *    widened exactly and narrowed round-to-nearest-even; a NaN narrows to
+ *    the quiet NaN 0x7FC0.
  */
 #ifndef LIONCUB_H
 #define LIONCUB_H

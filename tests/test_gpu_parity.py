@@ -237,6 +237,26 @@ def test_bf16_theta_decay_handworked_gpu():
     bf16_decay_run(gpu_step_fn())
 
 
+def test_bf16_theta_nan_narrows_to_quiet_nan_gpu():
+    """bf16 parameters that are NaN (any sign and payload) stay NaN through
+    the step and come back as the quiet NaN 0x7FC0; the finite ones equal
+    the oracle's."""
+    from synth.gen import to_bf16_bits
+    wl = wls.flat("nan", 300, W=3, theta_dtype="bf16", grad_dtype="bf16")
+    rs = np.random.default_rng(8)
+    theta = to_bf16_bits(rs.normal(0, 0.02, 300).astype(np.float32))
+    nans = np.array([0x7F81, 0xFF81, 0x7FC0, 0xFFC0, 0x7FFF, 0xFFFF, 0x7FA0], np.uint16)
+    theta[::43] = nans[: len(theta[::43])]
+    g = np.zeros((3, wl.ld), np.uint16)
+    g[:, :300] = to_bf16_bits(rs.normal(0, 1e-3, (3, 300)).astype(np.float32))
+    m = np.zeros((3, wl.ld), np.float32)
+    got = gpu_step_fn()(wl, theta, m, g, 1)["theta"]
+    want = theta.copy()
+    lco.step(wl, want, m.copy(), g.copy(), 1)
+    assert np.all(got[::43] == 0x7FC0)
+    assert np.array_equal(got, want)
+
+
 def test_identical_momenta_zero_spread_gpu():
     """64 identical workers: the largest inter-worker variance is exactly 0
     although its fp64 evaluation is negative for some columns."""
