@@ -410,8 +410,8 @@ double lco_minf(const float *x, int64_t n) {
  * measured against; the pages name it but print no formula, so this is the
  * reading of Eq. (1) with max |x| for M1 and stochastic rounding:
  * floor(y) + [u < y - floor(y)], y = (2^(n-1)-1)/max|x| * x in fp64,
- * u = r * 2^-32 for 32 random bits r (lco_sr_u32), clamped.  PARITY PARTLY
- * UNPINNED (the formula is a reading); pinned: integer y, the threshold's
+ * u = r * 2^-32 for 32 random bits r (lco_sr_u32), clamped.  The formula
+ * is a reading; each of its steps is pinned: integer y, the threshold's
  * direction, the clamp, unbiasedness, the pages' zero-collapse finding, and
  * which published generator output and half each element draws
  * (tests/golden/sr_draws.json). */

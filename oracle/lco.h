@@ -147,7 +147,7 @@ void lco_step_range(const lco_cfg *cfg, int64_t j0, int64_t j1,
                     int64_t ldc, int64_t t, const lco_debug *dbg);
 
 /* ---- max-norm (Q-infinity) stochastic quantisation: the baseline ------
- * PARITY PARTLY UNPINNED: the pages name this quantiser as the baseline
+ * A READING, PINNED STEP BY STEP: the pages name this quantiser as the baseline
  * that L1 replaces (Lion Cub review, Figure 4 caption: with stochastic
  * rounding it sends most entries to zero; the referee report on Eq. (1)
  * says the paper's section 2 defines that stochastic rounding) but never
@@ -158,8 +158,10 @@ void lco_step_range(const lco_cfg *cfg, int64_t j0, int64_t j1,
  * in fp64, u uniform in [0, 1) from the counter-based generator below.
  * Pinned: the generator's published first outputs, which output and half
  * an element draws (tuples worked by hand onto those published outputs),
- * exactness of max|x|, integer y (no randomness), unbiasedness E[q] = y,
- * and the pages' claim that on heavy-tailed updates most codes become 0. */
+ * exactness of max|x|, integer y (no randomness), the threshold's
+ * direction, the clamp, unbiasedness E[q] = y, and the pages' claim that on
+ * heavy-tailed updates most codes become 0.  What no pin can settle is
+ * whether the paper's quantiser is this formula: the pages do not print it. */
 
 /* SplitMix64 (Steele, Lea and Flood, 2014) used as a counter-based
  * generator: the counter-th output of the stream started at `seed`. */
