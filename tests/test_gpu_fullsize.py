@@ -115,8 +115,11 @@ def run_fullsize(wl, steps, tensors=None, n_random=6):
 
 def run_every_element(wl, steps):
     """The workload at its real size for its steps, every element of theta
-    and m (and every norm) compared with the oracle after every step; each
-    side carries its own state, the device's is never reset."""
+    and m (and every norm) compared with the oracle after every step.  The
+    oracle steps from the device's pre-step snapshot and the device state is
+    never reset; with every step required bit-equal, the device's trajectory
+    is the oracle's (test_independent_trajectory_at_full_size runs the two
+    apart on the workloads whose state fits in host memory)."""
     import torch
     from tests.fullsize_check import check_step_every_element
     torch.cuda.set_device(0)
@@ -140,6 +143,60 @@ def test_every_element_at_full_size(wl):
     and 3 steps): every parameter, every momentum of every worker, and on
     the L1 workloads the mean |c| of every (worker, tensor) pair."""
     run_every_element(wl, list(range(1, wl.steps + 1)))
+
+
+def _oracle_step_threaded(wl, theta, m, g, t, P=16):
+    """One oracle step (vote or averaging path: no norms) on host arrays in
+    place, its columns split over P threads on disjoint 64-aligned ranges
+    (a column's update reads and writes nothing outside it)."""
+    import ctypes as C
+    from concurrent.futures import ThreadPoolExecutor
+    L = lco.lib()
+    cfg = lco.OracleCfg(wl)
+    ld = m.shape[1]
+    per = (-(-wl.d // P) + 63) // 64 * 64
+    ranges = [(a, min(wl.d, a + per)) for a in range(0, wl.d, per)]
+
+    def run(r):
+        a, b = r
+        L.lco_step_range(cfg.ref, a, b, None, C.c_void_p(theta.ctypes.data + a * theta.itemsize),
+                         C.c_void_p(m.ctypes.data + a * m.itemsize),
+                         C.c_void_p(g.ctypes.data + a * g.itemsize), ld, t, None)
+    with ThreadPoolExecutor(P) as pool:
+        list(pool.map(run, ranges))
+
+
+@pytest.mark.parametrize("wl", [wls.FLAT_1M_W4_VOTE, wls.GPT2_124M_W8_VOTE], ids=lambda w: w.name)
+def test_independent_trajectory_at_full_size(wl):
+    """The 1M x 4 workload over its 10 steps and the GPT-2 small list
+    (124M x 8) over its 5, each side carrying its own theta and m from the
+    same seeded start: the oracle on host copies, the library on the device,
+    nothing passed from one to the other but each step's gradients.  Every
+    element is compared after every step and at the end."""
+    import torch
+    torch.cuda.set_device(0)
+    theta = gen.device_theta(wl)
+    m = gen.device_m(wl)
+    g = gen.device_g(wl, 1)
+    th_h, m_h = to_host(theta).copy(), to_host(m).copy()
+    lc = lioncub_for(wl)
+    tb = wl.theta_dtype == "bf16"
+    for t in range(1, wl.steps + 1):
+        gen.fill_device_g(wl, t, g)
+        torch.cuda.synchronize()
+        g_h = to_host(g)
+        lc.step(theta, m, g, t)
+        _oracle_step_threaded(wl, th_h, m_h, g_h, t)
+        torch.cuda.synchronize()
+        for name, got, want in ((f"theta t={t}", to_host(theta), th_h),
+                                (f"m t={t}", to_host(m)[:, : wl.d], m_h[:, : wl.d])):
+            u = np.uint16 if tb and name.startswith("theta") else np.uint32
+            if not np.array_equal(got.view(u), want.view(u)):     # the full bar says what differs
+                check_float_state(name, got, want, bf16=(u == np.uint16))
+        _say(wl.name, f"independent trajectories equal after step {t}")
+    lc.close()
+    del theta, m, g
+    torch.cuda.empty_cache()
 
 
 EXTRA_EVERY_ELEMENT = {
