@@ -125,3 +125,35 @@ def test_static_step_wrapper_matches_context_step():
     with pytest.raises(ValueError):
         st.step(s_theta[:-1], s_m, g, 3)
     lc.close()
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("wl", [wls.GPT_760M_W8_VOTE_SYNC, wls.GPT_1B3_W8_L1Q8],
+                         ids=lambda w: w.name)
+def test_static_step_full_size_tensor_lists(wl):
+    """The two 292-tensor GPT lists at full size (the tables rebuilt in
+    several launches of 32 tensor entries every call; the 1.3B list's
+    workspace, 44 MiB, is the largest of the workloads): two allocation-free
+    steps against two context steps on copies of the same device state,
+    theta and m bit-equal after each."""
+    import torch
+    torch.cuda.set_device(0)
+    theta, m = gen.device_theta(wl), gen.device_m(wl)
+    g = gen.device_g(wl, 1)
+    s_theta, s_m = theta.clone(), m.clone()
+    lc = lioncub_for(wl)
+    stream = torch.cuda.current_stream()
+
+    def bits(x):
+        return x.view(torch.int16) if x.dtype == torch.bfloat16 else x.view(torch.int32)
+    for t in (1, 2):
+        gen.fill_device_g(wl, t, g)
+        lc.step(theta, m, g, t)
+        _abi.lioncub_step_static(lc.cfg, _abi._stream_handle(stream), s_theta, s_m, g, t)
+        torch.cuda.synchronize()
+        assert torch.equal(bits(s_theta), bits(theta)), f"{wl.name} theta t={t}"
+        assert torch.equal(bits(s_m), bits(m)), f"{wl.name} m t={t}"
+        print("no-alloc full size", wl.name, "t", t, "bit-equal", flush=True)
+    lc.close()
+    del theta, m, g, s_theta, s_m
+    torch.cuda.empty_cache()
