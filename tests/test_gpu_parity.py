@@ -76,6 +76,14 @@ EDGE = {
     "row-padding-bf16g-avg-sync": wls.Workload(name="e20", tensors=[("wte", 192), ("h", 4096 + 5)],
                                                W=5, agg="avg", grad_dtype="bf16", ld_pad=64,
                                                sync_names=("wte",), sync_every=3),
+    # long tensor lists: 2,000 tensors of 64 to 4160 elements (tables built
+    # in 63 launches of 32 entries; block and group owners found by search)
+    "2000-tensors-vote": wls.Workload(name="e21", tensors=[(f"t{k}", 64 * (1 + k % 5) + (4096 if k % 97 == 0 else 0))
+                                                           for k in range(2000)],
+                                      W=3, sync_names=("t7", "t1999"), sync_every=2),
+    "2000-tensors-l1": wls.Workload(name="e22", tensors=[(f"t{k}", 64 * (1 + k % 7) + (4096 if k % 89 == 0 else 0))
+                                                         for k in range(2000)],
+                                    W=4, agg="l1", qbits=5),
 }
 
 

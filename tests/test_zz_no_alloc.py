@@ -22,6 +22,9 @@ CASES = [
     wls.Workload(name="na-l1-small", tensors=[("a", 9 * 4096 + 64), ("b", 4096), ("c", 832)],
                  W=5, agg="l1", qbits=4, sync_names=("a",), sync_every=2),
     wls.flat("na-vote", 3 * 4096 + 100, W=4, agg="vote", theta_dtype="bf16"),
+    # a long list after the short ones: 2,000 tensors, tables in 63 launches
+    wls.Workload(name="na-l1-2000", tensors=[(f"t{k}", 64 * (1 + k % 5)) for k in range(2000)],
+                 W=3, agg="l1", qbits=3),
 ]
 
 
@@ -50,7 +53,7 @@ def _compare_one(wl, t):
 
 
 def test_static_step_matches_context_step_calls_in_a_row():
-    for t, wl in zip((1, 2, 3), CASES):
+    for t, wl in zip((1, 2, 3, 5), CASES):
         print("no-alloc", wl.name, "d", wl.d, "W", wl.W, "t", t, flush=True)
         _compare_one(wl, t)
     # and back to the first, largest shape after the smaller ones
