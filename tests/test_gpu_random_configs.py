@@ -63,6 +63,39 @@ def test_random_config(k):
     gpu_step_vs_oracle(wl, steps=1, t0=t0 + 2, debug=False, seed_shift=1)
 
 
+def random_hyper_workload(k):
+    """A random configuration as above with random hyperparameters and value
+    scales, including the degenerate ones: beta1 = 1 (c = m) or 0 (c = g),
+    beta2 = 1 (m' = m) or 0 (m' = g), lr = 0 (theta unchanged), wd = 0 or
+    large, and parameters, momenta and gradients from 1e-30 (subnormal
+    products) to 1e3."""
+    rs = np.random.default_rng(7000 + k)
+    pick = lambda xs: xs[int(rs.integers(0, len(xs)))]
+    return random_workload(k).with_(
+        name=f"hyper{k}",
+        beta1=pick([0.9, 0.5, 0.0, 1.0, float(np.float32(rs.random()))]),
+        beta2=pick([0.99, 0.95, 0.0, 1.0, float(np.float32(rs.random()))]),
+        lr=pick([1e-4, 1e-2, 0.5, 0.0, float(np.float32(rs.random() * 1e-3))]),
+        wd=pick([0.1, 0.0, 1.0, float(np.float32(rs.random()))]),
+        theta_std=pick([0.02, 1e3, 1e-20]),
+        m_std=pick([1e-3, 1.0, 1e-30]),
+        g_scale=pick([1e-3, 1e2, 1e-30]),
+        g_tensor_scale=None)
+
+
+N_HYPER = int(os.environ.get("LIONCUB_RANDOM_HYPER", "60"))
+
+
+@pytest.mark.parametrize("k", range(N_HYPER))
+def test_random_hyperparameters(k):
+    wl = random_hyper_workload(k)
+    t0 = int(np.random.default_rng(50_000 + k).integers(1, 1000))
+    print(wl.name, wl.agg, "W", wl.W, "n", wl.qbits, "beta", wl.beta1, wl.beta2, "lr", wl.lr,
+          "wd", wl.wd, "scales", wl.theta_std, wl.m_std, wl.g_scale, "t0", t0, flush=True)
+    gpu_step_vs_oracle(wl, steps=2, t0=t0, debug=True)
+    gpu_step_vs_oracle(wl, steps=1, t0=t0 + 2, debug=False, seed_shift=1)
+
+
 N_EXCHANGE = 40
 
 
