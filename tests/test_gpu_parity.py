@@ -95,6 +95,20 @@ def test_edge_parity(name, debug):
     print(name, res, flush=True)
 
 
+@pytest.mark.parametrize("t0", [2**62 - 1, 2**63 - 4], ids=["t=2^62-1", "t=2^63-4"])
+def test_max_norm_counter_wraps(t0):
+    """Step indices near 2^62 and 2^63: the max-norm draws' counter
+    (t*W + i)*d + 2*floor(j/2) wraps modulo 2^64 on both sides (the
+    wrap-around itself is pinned on the oracle by tuples landing on the
+    generator's published outputs); the vote path's parity at the same t."""
+    for wl in (wls.flat("wrap-linf", 3 * 4096 + 100, W=5, agg="linf", qbits=4),
+               wls.Workload(name="wrap-linf-tensors", tensors=[("a", 4096 + 64), ("b", 704)], W=3,
+                            agg="linf", qbits=7, grad_dtype="bf16"),
+               wls.flat("wrap-vote", 4096 + 36, W=4, tie="zero")):
+        res = gpu_step_vs_oracle(wl, steps=2, t0=t0)
+        print(wl.name, t0, res, flush=True)
+
+
 def test_vote_tie_rate_on_gpu():
     """Majority ties at W=4 occur for over 30% of parameters (the pages'
     observation; C(4,2)/16 = 0.375 for symmetric iid c)."""
